@@ -1,0 +1,174 @@
+"""Block-manager model (test infrastructure only; see ``oracle/__init__``).
+
+Follows [p2] "PagedAttention: KV cache as virtual memory", sections "Direct
+answer" and "Deep dive", and [p3] "PagedAttention: Why Static Batching Wastes
+Your KV Cache", sections "What does PagedAttention actually do differently?"
+and "How does copy-on-write eliminate duplicate prompt KV cache?":
+
+* one shared pool of fixed-size physical blocks; free blocks sit in a queue,
+  allocation takes from the front and freeing appends at the back;
+* each block carries a reference count; a block goes back to the queue when its
+  count reaches zero;
+* each sequence owns a block table (logical block index -> physical block id);
+  a block is taken only when the sequence grows past a block boundary;
+* forking a sequence shares every block (count + 1 each), like ``fork()``;
+* writing new tokens into a shared, partly filled last block first copies that
+  one block to a fresh one and repoints the table entry (copy-on-write).
+
+Readings where the pages are silent (stated in the design notes as well):
+
+* the initial queue order is 0..N-1 unless an explicit order is given;
+* freeing a sequence walks its table in logical order, appending each block whose
+  count drops to zero;
+* inside one append the copy-on-write block is taken first, then new blocks in
+  increasing logical index;
+* copy-on-write fires only when tokens land in an existing partial last block
+  whose count is above one; the last holder writes in place;
+* every call is all-or-nothing: on any error the state is unchanged.
+"""
+
+from __future__ import annotations
+
+import collections
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+class Status:
+    OK = "ok"
+    NO_BLOCKS = "no_blocks"
+    BAD_SEQ = "bad_seq"
+    BAD_ARG = "bad_arg"
+    CAPACITY = "capacity"
+
+
+class OraclePool:
+    def __init__(self, num_blocks: int, block_size: int = 16,
+                 init_free_order: Optional[Sequence[int]] = None):
+        if num_blocks < 1 or block_size < 1:
+            raise ValueError("bad pool shape")
+        if init_free_order is None:
+            order = list(range(num_blocks))
+        else:
+            order = [int(x) for x in init_free_order]
+            if sorted(order) != list(range(num_blocks)):
+                raise ValueError("init_free_order must be a permutation of 0..N-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = collections.deque(order)
+        self.ref_cnt: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+        self.next_seq = 0
+        self.cow_copies = 0
+
+    # -- sequences -------------------------------------------------------
+    def seq_create(self) -> Tuple[str, int]:
+        sid = self.next_seq
+        self.next_seq += 1
+        self.tables[sid] = []
+        self.lens[sid] = 0
+        return Status.OK, sid
+
+    def alloc_append(self, sid: int, n: int):
+        """Reserve room for ``n`` new tokens of sequence ``sid``.
+
+        Returns ``(status, slots, cow)`` where ``slots[i]`` is the flat cache
+        slot (physical block * block_size + offset) of token ``len + i`` and
+        ``cow`` is ``(src, dst)`` when a shared partial block was copied, else
+        ``None``.
+        """
+        if sid not in self.tables:
+            return Status.BAD_SEQ, [], None
+        if n < 0:
+            return Status.BAD_ARG, [], None
+        bs = self.block_size
+        table = self.tables[sid]
+        length = self.lens[sid]
+        if n == 0:
+            return Status.OK, [], None
+        # blocks the sequence must hold after the append (one per started block)
+        blocks_after = (length + n + bs - 1) // bs
+        new_blocks = blocks_after - len(table)
+        partial_last = (length % bs) != 0
+        cow = partial_last and self.ref_cnt[table[-1]] > 1
+        need = new_blocks + (1 if cow else 0)
+        if need > len(self.free):
+            return Status.NO_BLOCKS, [], None
+        cow_pair = None
+        if cow:
+            src = table[-1]
+            dst = self.free.popleft()
+            self.ref_cnt[src] -= 1
+            self.ref_cnt[dst] = 1
+            table[-1] = dst
+            cow_pair = (src, dst)
+            self.cow_copies += 1
+        for _ in range(new_blocks):
+            b = self.free.popleft()
+            self.ref_cnt[b] = 1
+            table.append(b)
+        slots = []
+        for i in range(n):
+            pos = length + i
+            slots.append(table[pos // bs] * bs + pos % bs)
+        self.lens[sid] = length + n
+        return Status.OK, slots, cow_pair
+
+    def fork(self, parent: int) -> Tuple[str, int]:
+        if parent not in self.tables:
+            return Status.BAD_SEQ, -1
+        sid = self.next_seq
+        self.next_seq += 1
+        self.tables[sid] = list(self.tables[parent])
+        self.lens[sid] = self.lens[parent]
+        for b in self.tables[sid]:
+            self.ref_cnt[b] += 1
+        return Status.OK, sid
+
+    def seq_free(self, sid: int) -> str:
+        if sid not in self.tables:
+            return Status.BAD_SEQ
+        for b in self.tables[sid]:
+            self.ref_cnt[b] -= 1
+            if self.ref_cnt[b] == 0:
+                self.free.append(b)
+        del self.tables[sid]
+        del self.lens[sid]
+        return Status.OK
+
+    # -- export ------------------------------------------------------------
+    def block_tables(self, sids: Sequence[int], max_blocks: int):
+        """Padded ``[len(sids)][max_blocks]`` table (pad -1) and lengths."""
+        for s in sids:
+            if s not in self.tables:
+                return Status.BAD_SEQ, None, None
+            if len(self.tables[s]) > max_blocks:
+                return Status.CAPACITY, None, None
+        rows, lens = [], []
+        for s in sids:
+            t = self.tables[s]
+            rows.append(list(t) + [-1] * (max_blocks - len(t)))
+            lens.append(self.lens[s])
+        return Status.OK, rows, lens
+
+    def stats(self) -> Dict[str, int]:
+        free = len(self.free)
+        tokens = sum(self.lens.values())
+        waste = sum(len(self.tables[s]) * self.block_size - self.lens[s] for s in self.tables)
+        return {
+            "num_blocks": self.num_blocks,
+            "free_blocks": free,
+            "used_blocks": self.num_blocks - free,
+            "shared_blocks": sum(1 for c in self.ref_cnt if c > 1),
+            "total_refs": sum(self.ref_cnt),
+            "cow_copies": self.cow_copies,
+            "live_seqs": len(self.tables),
+            "tokens": tokens,
+            "waste_tokens": waste,
+        }
+
+    def free_order(self) -> List[int]:
+        return list(self.free)
+
+    def table(self, sid: int) -> List[int]:
+        return list(self.tables[sid])

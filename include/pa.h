@@ -1,0 +1,219 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The library follows the block-manager model of the pages:
+ *   [p1] "vLLM PagedAttention Deep Dive: KV Cache Memory Fragmentation, Chunked
+ *        Prefill & Prefix Caching"
+ *   [p2] "PagedAttention: KV cache as virtual memory (block manager & fragmentation)"
+ *   [p3] "PagedAttention: Why Static Batching Wastes Your KV Cache"
+ * A pool of fixed-size physical blocks is shared by all sequences; each sequence
+ * maps its logical blocks to physical blocks through a block table; blocks are
+ * taken one at a time as a sequence grows, returned when their reference count
+ * drops to zero, shared between forked sequences and copied per block on write.
+ * Attention reads K/V through the block table from scattered blocks.
+ *
+ * Conventions
+ * -----------
+ * Ownership.  A pool (pa_pool) holds host bookkeeping only.  Every device pointer
+ *   (caches, q, out, tables, slots, lens, workspace) is allocated and owned by the
+ *   caller.  The library never allocates or frees device memory and never
+ *   synchronises a stream.  hip_stream is a hipStream_t (NULL = the null stream).
+ * Errors.  Every call returns a pa_status; pa_last_error() gives a message for the
+ *   calling thread.  Host calls are all-or-nothing: on any non-OK status the pool
+ *   is bit-identical to its state before the call.  Device calls check their
+ *   arguments on the host and return PA_ERR_HIP if a launch fails; faults during
+ *   execution surface at the caller's next synchronisation.
+ * Threads.  A pool is used by one thread at a time (no internal locking).
+ * Limits.  block_size * num_blocks < 2^31 (slots are int32).  Device byte offsets
+ *   are computed in 64 bits.
+ * Device input checks.  Kernels never read or write outside the buffers the sizes
+ *   describe: slots outside [0, num_blocks*block_size) are skipped, context lengths
+ *   are clamped to [0, max_blocks*block_size], block ids outside [0, num_blocks)
+ *   are read as block 0.  Results for such inputs are unspecified but safe.
+ *
+ * Cache layout (the pages leave it open; chosen here).  K and V are two separate
+ *   device arrays, each [num_blocks][num_kv_heads][block_size][head_dim]: one
+ *   (block, head) is a contiguous block_size*head_dim tile (4 KiB for 16 x 128
+ *   fp16, 2 KiB for e4m3).  Token t of a sequence is row t % block_size of physical
+ *   block table[t / block_size]; its flat slot is block * block_size + row.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+#define PA_OK 0
+#define PA_ERR_NO_BLOCKS 1   /* not enough free blocks; nothing was taken        */
+#define PA_ERR_BAD_SEQ 2     /* unknown (or already freed) sequence id            */
+#define PA_ERR_BAD_ARG 3     /* null pointer, negative size, bad shape or order   */
+#define PA_ERR_CAPACITY 4    /* an output buffer is too small for the request     */
+#define PA_ERR_HIP 5         /* a HIP launch or copy reported an error            */
+#define PA_ERR_UNSUPPORTED 6 /* shape / dtype combination not compiled in         */
+
+#define PA_KV_F16 0          /* IEEE binary16                                     */
+#define PA_KV_FP8_E4M3 1     /* OCP 8-bit E4M3 (bias 7, max 448, no inf), scaled */
+
+typedef struct pa_pool pa_pool;
+
+/* Device-side description of one layer's paged K/V cache (caller-owned). */
+typedef struct {
+  void *k_cache;          /* [num_blocks][num_kv_heads][block_size][head_dim]        */
+  void *v_cache;          /* same shape as k_cache                                   */
+  int32_t num_blocks;
+  int32_t block_size;     /* tokens per block; the kernels are built for 16          */
+  int32_t num_kv_heads;
+  int32_t head_dim;       /* 64 or 128                                               */
+  int32_t dtype;          /* PA_KV_F16 or PA_KV_FP8_E4M3                             */
+  float k_scale;          /* e4m3 only: stored code * k_scale = value                */
+  float v_scale;          /* e4m3 only                                               */
+} pa_kv_cache;
+
+typedef struct {
+  int64_t num_blocks;
+  int64_t free_blocks;
+  int64_t used_blocks;    /* num_blocks - free_blocks                                */
+  int64_t shared_blocks;  /* blocks with ref_cnt > 1                                 */
+  int64_t total_refs;     /* sum of ref_cnt                                          */
+  int64_t cow_copies;     /* copy-on-write copies made since creation                */
+  int64_t live_seqs;
+  int64_t tokens;         /* sum of live sequence lengths                            */
+  int64_t waste_tokens;   /* sum over live sequences of blocks*block_size - length   */
+} pa_pool_stats;
+
+/* ---------------------------------------------------------------- host side -- */
+
+/* Create a pool of num_blocks physical blocks of block_size tokens ([p2] "Direct
+ * answer" and "Deep dive": one shared pool, a free queue with O(1) take-from-front
+ * and return-to-back).  init_free_order: NULL for 0..N-1, else a host array that is
+ * a permutation of 0..N-1 giving the initial queue order (copied).
+ * Errors: BAD_ARG for num_blocks < 1, block_size < 1, N*block_size >= 2^31, a
+ * non-permutation order or out == NULL. */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t *init_free_order, pa_pool **out);
+
+/* Release the pool's host memory.  NULL is ignored. */
+void pa_pool_destroy(pa_pool *pool);
+
+/* New empty sequence (length 0, empty table).  Ids are 0, 1, 2, ... in creation
+ * order and are never reused. */
+pa_status pa_seq_create(pa_pool *pool, int32_t *seq_out);
+
+/* Make room for n_tokens new tokens of sequence seq ([p2] "Deep dive", lifecycle:
+ * blocks are popped when the prompt is admitted and one more each time the last
+ * block fills; [p3] "What does PagedAttention actually do differently?": blocks
+ * are taken on demand, one per 16-token boundary).
+ * If the last block is partly filled and shared (ref_cnt > 1), it is first
+ * replaced by a fresh copy ([p3] "How does copy-on-write eliminate duplicate
+ * prompt KV cache?"): a block d is popped, table[last] = d, ref_cnt of the old
+ * block drops by one, and cow_out = {old, d}; otherwise cow_out = {-1, -1}.  The
+ * caller passes the pair to pa_write_kv, which copies the block's K/V on the device.
+ * Then ceil((len + n)/bs) - ceil(len/bs) blocks are popped (front of the queue, in
+ * logical order) and slots_out[i] = table[(len+i)/bs]*bs + (len+i)%bs.
+ * slots_out: host int32[n_tokens] (may be NULL if n_tokens == 0).  cow_out: host
+ * int32[2] or NULL (then a copy-on-write is refused with BAD_ARG).
+ * Errors: BAD_SEQ, BAD_ARG (n_tokens < 0, null pointer), NO_BLOCKS (fewer free
+ * blocks than needed, copy included); nothing changes on error. */
+pa_status pa_alloc_append(pa_pool *pool, int32_t seq, int32_t n_tokens,
+                          int32_t *slots_out, int32_t *cow_out);
+
+/* Fork: a new sequence whose table and length equal the parent's; every shared
+ * block's ref_cnt grows by one ([p1] "Virtual Memory Paging Analogy" on sharing;
+ * [p3] copy-on-write section: one copy of the prompt KV, like fork()).
+ * Errors: BAD_SEQ, BAD_ARG (child_out NULL). */
+pa_status pa_fork_cow(pa_pool *pool, int32_t parent, int32_t *child_out);
+
+/* Finish a sequence: for each block in logical order ref_cnt drops by one and a
+ * block reaching zero is appended to the back of the free queue ([p2] "Deep dive").
+ * Errors: BAD_SEQ. */
+pa_status pa_seq_free(pa_pool *pool, int32_t seq);
+
+/* Export block tables for n sequences as a host int32[n][max_blocks] array padded
+ * with -1, and lens_out int32[n] (may be NULL).  The caller copies them to the
+ * device.  Errors: BAD_SEQ, BAD_ARG, CAPACITY (a table longer than max_blocks). */
+pa_status pa_block_tables(const pa_pool *pool, const int32_t *seqs, int32_t n,
+                          int32_t max_blocks, int32_t *tables_out, int32_t *lens_out);
+
+/* Copy the table of one sequence (host int32[cap]); *n_out = its length in blocks.
+ * Errors: BAD_SEQ, CAPACITY. */
+pa_status pa_seq_table(const pa_pool *pool, int32_t seq, int32_t *table_out, int32_t cap,
+                       int32_t *n_out, int32_t *len_out);
+
+/* Snapshot of the pool: counters, and optionally the free queue from front to back
+ * (host int32[num_blocks], first free_blocks entries valid) and ref_cnt
+ * (host int32[num_blocks]).  Either array may be NULL. */
+pa_status pa_pool_state(const pa_pool *pool, pa_pool_stats *stats_out,
+                        int32_t *free_order_out, int32_t *ref_cnt_out);
+
+/* --------------------------------------------------------------- device side -- */
+
+/* Write new tokens' K/V into their slots (the K/V of each processed chunk is
+ * accumulated in paged blocks: [p1] "Mechanics of Chunked Prefill").
+ * First, for each of the n_cow pairs {src, dst} (host int32[n_cow][2], as returned
+ * by pa_alloc_append) the whole block src is copied to dst in both caches.  Then
+ * token i (0 <= i < T) is scattered: cache[slot/bs][h][slot%bs][:] = new[i][h][:]
+ * for every KV head h.  k_new, v_new: device fp16 [T][num_kv_heads][head_dim],
+ * contiguous.  slots_dev: device int32[T]; negative slots are padding and skipped.
+ * For e4m3 caches each value is stored as encode(clamp(x / scale, +-448)) with one
+ * correctly rounded fp32 division and round-to-nearest-even.
+ * All work is enqueued on hip_stream in that order.
+ * Errors: BAD_ARG (null pointers with T > 0, bad pairs, bad descriptor),
+ * UNSUPPORTED (dtype / block_size), HIP. */
+pa_status pa_write_kv(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                      const int32_t *slots_dev, int32_t T,
+                      const int32_t *cow_pairs_host, int32_t n_cow, void *hip_stream);
+
+/* Bytes of device workspace pa_decode needs for this shape (split-K partials). */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len);
+
+/* Decode attention: one query per sequence over its paged context ([p1]
+ * "PagedAttention Mechanism": look the physical blocks up in the block table,
+ * gather K/V, run standard attention; [p2]/[p3]: the result equals attention over
+ * the same tokens stored contiguously).
+ * out[b][h] = softmax(scale * K_b q[b][h]) V_b over tokens 0..lens[b]-1 of KV head
+ * h / (num_heads / num_kv_heads).  Sequences with lens[b] == 0 get zeros.
+ * q: device fp16 [B][num_heads][head_dim].  tables_dev: device int32[B][max_blocks]
+ * (as from pa_block_tables).  lens_dev: device int32[B].  max_context_len: an upper
+ * bound on every lens[b] (sizes the split-K grid).  out_dev: device fp32
+ * [B][num_heads][head_dim].  workspace: at least pa_decode_workspace_bytes(...).
+ * Errors: BAD_ARG (shape, null pointers, num_heads % num_kv_heads, workspace too
+ * small), UNSUPPORTED (block_size != 16, head_dim not 64/128), HIP. */
+pa_status pa_decode(const pa_kv_cache *cache, const void *q, int32_t num_heads,
+                    const int32_t *tables_dev, const int32_t *lens_dev, int32_t B,
+                    int32_t max_blocks, int32_t max_context_len, float scale,
+                    float *out_dev, void *workspace_dev, size_t workspace_bytes,
+                    void *hip_stream);
+
+/* Chunked-prefill attention over the paged cache ([p1] "Chunked Prefill" and
+ * "Mechanics of Chunked Prefill"): the chunk's K/V must already be written (by
+ * pa_write_kv).  Sequence b owns query rows cu_q[b] .. cu_q[b+1]-1; row i of it sits
+ * at absolute position prior[b] + i and attends to tokens 0 .. prior[b] + i (causal
+ * inside the chunk, everything before it).
+ * q: device fp16 [total_q_rows][num_heads][head_dim] (total_q_rows = cu_q[B]; rows at
+ * or beyond it are never read or written).  cu_q_dev: device int32[B+1],
+ * non-decreasing, cu_q[0] = 0.  prior_dev: device int32[B].  tables_dev: device
+ * int32[B][max_blocks].  max_chunk: upper bound on cu_q[b+1] - cu_q[b].  out_dev:
+ * device fp32 [total_q_rows][num_heads][head_dim].
+ * Errors: BAD_ARG, UNSUPPORTED (block_size != 16, head_dim not 64/128, e4m3 cache), HIP. */
+pa_status pa_prefill_chunk(const pa_kv_cache *cache, const void *q, int32_t num_heads,
+                           int32_t total_q_rows, const int32_t *cu_q_dev, const int32_t *prior_dev,
+                           const int32_t *tables_dev, int32_t B, int32_t max_blocks,
+                           int32_t max_chunk, float scale, float *out_dev, void *hip_stream);
+
+/* Message describing the last non-OK status on the calling thread ("" if none). */
+const char *pa_last_error(void);
+
+/* Library version string. */
+const char *pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

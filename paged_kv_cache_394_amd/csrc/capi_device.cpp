@@ -1,0 +1,143 @@
+// C ABI: device-side entry points.  Each call checks its arguments on the host,
+// then enqueues the kernels on the caller's stream.  Declared in include/pa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "launch.hpp"
+#include "pa.h"
+#include "status.hpp"
+
+using pa::fail;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a cache descriptor; fills *d.  Returns PA_OK or an error status.
+pa_status check_cache(const pa_kv_cache* c, const char* fn, pa::KvDesc* d) {
+  const std::string f(fn);
+  if (c == nullptr) return fail(PA_ERR_BAD_ARG, f + ": cache is NULL");
+  if (c->k_cache == nullptr || c->v_cache == nullptr)
+    return fail(PA_ERR_BAD_ARG, f + ": k_cache / v_cache is NULL");
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache))
+    return fail(PA_ERR_BAD_ARG, f + ": caches must be 16-byte aligned");
+  if (c->num_blocks < 1 || c->num_kv_heads < 1)
+    return fail(PA_ERR_BAD_ARG, f + ": num_blocks and num_kv_heads must be >= 1");
+  if (static_cast<int64_t>(c->num_blocks) * 16 >= (int64_t(1) << 31))
+    return fail(PA_ERR_BAD_ARG, f + ": num_blocks * 16 must be < 2^31");
+  if (c->block_size != 16) return fail(PA_ERR_UNSUPPORTED, f + ": kernels are built for block_size 16");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (c->dtype != PA_KV_F16 && c->dtype != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_BAD_ARG, f + ": unknown cache dtype");
+  const bool fp8 = c->dtype == PA_KV_FP8_E4M3;
+  if (fp8 && !(std::isfinite(c->k_scale) && c->k_scale > 0.f && std::isfinite(c->v_scale) &&
+               c->v_scale > 0.f))
+    return fail(PA_ERR_BAD_ARG, f + ": e4m3 scales must be finite and > 0");
+  *d = pa::KvDesc{c->k_cache, c->v_cache, c->num_blocks, c->block_size, c->num_kv_heads,
+                  c->head_dim, fp8, fp8 ? c->k_scale : 1.f, fp8 ? c->v_scale : 1.f};
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string(fn) + ": " + hipGetErrorString(e));
+  return pa::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new,
+                      const int32_t* slots_dev, int32_t T, const int32_t* cow_pairs_host,
+                      int32_t n_cow, void* hip_stream) {
+  const char* fn = "pa_write_kv";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  if (T < 0 || n_cow < 0) return fail(PA_ERR_BAD_ARG, "pa_write_kv: negative count");
+  if (T > 0 && (k_new == nullptr || v_new == nullptr || slots_dev == nullptr))
+    return fail(PA_ERR_BAD_ARG, "pa_write_kv: NULL k_new / v_new / slots");
+  if (T > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(PA_ERR_BAD_ARG, "pa_write_kv: k_new / v_new must be 16-byte aligned");
+  if (static_cast<int64_t>(T) * d.num_kv_heads * (d.head_dim / 8) >= (int64_t(1) << 31) * 256)
+    return fail(PA_ERR_BAD_ARG, "pa_write_kv: too many tokens for one launch");
+  if (n_cow > 0) {
+    if (cow_pairs_host == nullptr) return fail(PA_ERR_BAD_ARG, "pa_write_kv: NULL cow pairs");
+    for (int32_t i = 0; i < n_cow; ++i) {
+      const int32_t s = cow_pairs_host[2 * i], t = cow_pairs_host[2 * i + 1];
+      if (s < 0 || s >= d.num_blocks || t < 0 || t >= d.num_blocks || s == t)
+        return fail(PA_ERR_BAD_ARG, "pa_write_kv: cow pair out of range");
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (n_cow > 0) {
+    const hipError_t e = pa::launch_copy_blocks(d, cow_pairs_host, n_cow, s);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return hip_status(pa::launch_write_kv(d, k_new, v_new, slots_dev, T, s), fn);
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len) {
+  return pa::decode_workspace_bytes(B, num_heads, head_dim, max_context_len);
+}
+
+pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
+                    const int32_t* tables_dev, const int32_t* lens_dev, int32_t B,
+                    int32_t max_blocks, int32_t max_context_len, float scale, float* out_dev,
+                    void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+  const char* fn = "pa_decode";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
+    return fail(PA_ERR_BAD_ARG, "pa_decode: num_heads must be a positive multiple of num_kv_heads");
+  if (B < 0 || max_blocks < 1 || max_context_len < 0)
+    return fail(PA_ERR_BAD_ARG, "pa_decode: bad B / max_blocks / max_context_len");
+  if (B == 0) return pa::ok();
+  if (q == nullptr || tables_dev == nullptr || lens_dev == nullptr || out_dev == nullptr)
+    return fail(PA_ERR_BAD_ARG, "pa_decode: NULL device pointer");
+  if (!aligned16(q) || !aligned16(out_dev)) return fail(PA_ERR_BAD_ARG, "pa_decode: q / out must be 16-byte aligned");
+  if (num_heads > 65535 || B > 65535) return fail(PA_ERR_BAD_ARG, "pa_decode: num_heads and B must be <= 65535");
+  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, "pa_decode: scale must be finite");
+  const size_t need = pa::decode_workspace_bytes(B, num_heads, d.head_dim, max_context_len);
+  if (workspace_bytes < need || (need > 0 && workspace_dev == nullptr))
+    return fail(PA_ERR_BAD_ARG, "pa_decode: workspace smaller than pa_decode_workspace_bytes()");
+  if (need > 0 && !aligned16(workspace_dev))
+    return fail(PA_ERR_BAD_ARG, "pa_decode: workspace must be 16-byte aligned");
+  return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, B, max_blocks,
+                                      max_context_len, scale, out_dev, workspace_dev,
+                                      static_cast<hipStream_t>(hip_stream)),
+                    fn);
+}
+
+pa_status pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t num_heads,
+                           int32_t total_q_rows, const int32_t* cu_q_dev, const int32_t* prior_dev,
+                           const int32_t* tables_dev, int32_t B, int32_t max_blocks,
+                           int32_t max_chunk, float scale, float* out_dev, void* hip_stream) {
+  const char* fn = "pa_prefill_chunk";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  if (d.fp8) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: e4m3 caches are decode-only");
+  if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
+    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: num_heads must be a positive multiple of num_kv_heads");
+  if (B < 0 || max_blocks < 1 || max_chunk < 0 || total_q_rows < 0)
+    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: bad B / max_blocks / max_chunk / total_q_rows");
+  if (B == 0 || total_q_rows == 0 || max_chunk == 0) return pa::ok();
+  if (q == nullptr || cu_q_dev == nullptr || prior_dev == nullptr || tables_dev == nullptr ||
+      out_dev == nullptr)
+    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: NULL device pointer");
+  if (!aligned16(q) || !aligned16(out_dev))
+    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: q / out must be 16-byte aligned");
+  if (num_heads > 65535 || B > 65535)
+    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: num_heads and B must be <= 65535");
+  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: scale must be finite");
+  return hip_status(pa::launch_prefill(d, q, num_heads, total_q_rows, cu_q_dev, prior_dev,
+                                       tables_dev, B, max_blocks, max_chunk, scale, out_dev,
+                                       static_cast<hipStream_t>(hip_stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per kernel
+// family).  Arguments are validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+struct KvDesc {
+  void* k;
+  void* v;
+  int32_t num_blocks, block_size, num_kv_heads, head_dim;
+  bool fp8;
+  float k_scale, v_scale;
+};
+
+// Copy whole blocks src -> dst in both caches; pairs: host int32[n][2].
+hipError_t launch_copy_blocks(const KvDesc& c, const int32_t* pairs, int32_t n, hipStream_t s);
+
+// Scatter T tokens' K/V rows to their slots.
+hipError_t launch_write_kv(const KvDesc& c, const void* k_new, const void* v_new,
+                           const int32_t* slots, int32_t T, hipStream_t s);
+
+// Split-K decode: partition kernel + partition reduce.
+int32_t decode_partition_tokens();
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len);
+hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
+                         const int32_t* lens, int32_t B, int32_t max_blocks, int32_t max_context_len,
+                         float scale, float* out, void* workspace, hipStream_t s);
+
+// Chunked prefill (MFMA).
+hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,
+                          const int32_t* cu_q, const int32_t* prior, const int32_t* tables,
+                          int32_t B, int32_t max_blocks, int32_t max_chunk, float scale, float* out,
+                          hipStream_t s);
+
+}  // namespace pa

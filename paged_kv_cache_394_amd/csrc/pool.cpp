@@ -1,0 +1,263 @@
+// Host block manager; see pool.hpp for the model and its sources.
+#include "pool.hpp"
+
+#include <new>
+
+namespace pa {
+
+namespace {
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+BlockPool::BlockPool(int32_t n, int32_t bs)
+    : n_(n), bs_(bs), next_(n, -1), prev_(n, -1), in_queue_(n, 0), ref_(n, 0) {}
+
+Status BlockPool::create(int32_t num_blocks, int32_t block_size, const int32_t* order,
+                         BlockPool** out, std::string* err) {
+  if (out == nullptr) {
+    *err = "pa_pool_create: out is NULL";
+    return kBadArg;
+  }
+  if (num_blocks < 1 || block_size < 1) {
+    *err = "pa_pool_create: num_blocks and block_size must be >= 1";
+    return kBadArg;
+  }
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t(1) << 31)) {
+    *err = "pa_pool_create: num_blocks * block_size must be < 2^31 (slots are int32)";
+    return kBadArg;
+  }
+  BlockPool* p = nullptr;
+  try {
+    p = new BlockPool(num_blocks, block_size);
+  } catch (const std::bad_alloc&) {
+    *err = "pa_pool_create: out of host memory";
+    return kBadArg;
+  }
+  if (order != nullptr) {
+    std::vector<uint8_t> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        *err = "pa_pool_create: init_free_order is not a permutation of 0..num_blocks-1";
+        return kBadArg;
+      }
+      seen[b] = 1;
+    }
+  }
+  for (int32_t i = 0; i < num_blocks; ++i) p->push_back(order ? order[i] : i);
+  *out = p;
+  return kOk;
+}
+
+int32_t BlockPool::pop_front() {
+  const int32_t b = head_;
+  head_ = next_[b];
+  if (head_ >= 0) prev_[head_] = -1; else tail_ = -1;
+  next_[b] = prev_[b] = -1;
+  in_queue_[b] = 0;
+  --nfree_;
+  return b;
+}
+
+void BlockPool::push_back(int32_t b) {
+  prev_[b] = tail_;
+  next_[b] = -1;
+  if (tail_ >= 0) next_[tail_] = b; else head_ = b;
+  tail_ = b;
+  in_queue_[b] = 1;
+  ++nfree_;
+}
+
+Status BlockPool::seq_create(int32_t* id) {
+  if (id == nullptr) return kBadArg;
+  if (seqs_.size() >= static_cast<size_t>(INT32_MAX)) return kCapacity;
+  try {
+    seqs_.emplace_back();
+  } catch (const std::bad_alloc&) {
+    return kCapacity;
+  }
+  seqs_.back().live = true;
+  *id = static_cast<int32_t>(seqs_.size() - 1);
+  ++live_seqs_;
+  return kOk;
+}
+
+Status BlockPool::alloc_append(int32_t seq, int32_t n, int32_t* slots, int32_t* cow,
+                               std::string* err) {
+  if (!live(seq)) {
+    *err = "pa_alloc_append: unknown sequence";
+    return kBadSeq;
+  }
+  if (n < 0) {
+    *err = "pa_alloc_append: n_tokens < 0";
+    return kBadArg;
+  }
+  if (n > 0 && slots == nullptr) {
+    *err = "pa_alloc_append: slots_out is NULL";
+    return kBadArg;
+  }
+  Seq& s = seqs_[seq];
+  if (cow != nullptr) cow[0] = cow[1] = -1;
+  if (n == 0) return kOk;
+  const int64_t len = s.len;
+  const int64_t nb = static_cast<int64_t>(s.table.size());
+  const int64_t blocks_after = ceil_div(len + n, bs_);
+  if (blocks_after * bs_ >= (int64_t(1) << 31)) {
+    *err = "pa_alloc_append: sequence would exceed 2^31 tokens";
+    return kBadArg;
+  }
+  const int64_t new_blocks = blocks_after - nb;
+  // copy-on-write: tokens will land in a partly filled last block that others share
+  const bool do_cow = (len % bs_) != 0 && ref_[s.table.back()] > 1;
+  if (do_cow && cow == nullptr) {
+    *err = "pa_alloc_append: copy-on-write needed but cow_out is NULL";
+    return kBadArg;
+  }
+  const int64_t need = new_blocks + (do_cow ? 1 : 0);
+  if (need > nfree_) {
+    *err = "pa_alloc_append: not enough free blocks";
+    return kNoBlocks;
+  }
+  try {
+    s.table.reserve(static_cast<size_t>(blocks_after));
+  } catch (const std::bad_alloc&) {
+    *err = "pa_alloc_append: out of host memory";
+    return kCapacity;
+  }
+  // --- no failure past this point ---
+  const int64_t waste_before = nb * bs_ - len;
+  if (do_cow) {
+    const int32_t src = s.table.back();
+    const int32_t dst = pop_front();
+    if (ref_[src] == 2) --shared_;
+    --ref_[src];
+    ref_[dst] = 1;
+    s.table.back() = dst;
+    cow[0] = src;
+    cow[1] = dst;
+    ++cow_copies_;
+  }
+  for (int64_t j = 0; j < new_blocks; ++j) {
+    const int32_t b = pop_front();
+    ref_[b] = 1;
+    ++refs_;
+    s.table.push_back(b);
+  }
+  const int32_t* tbl = s.table.data();
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t pos = len + i;
+    slots[i] = tbl[pos / bs_] * bs_ + static_cast<int32_t>(pos % bs_);
+  }
+  s.len = len + n;
+  tokens_ += n;
+  waste_ += (blocks_after * bs_ - s.len) - waste_before;
+  return kOk;
+}
+
+Status BlockPool::fork(int32_t parent, int32_t* child) {
+  if (!live(parent)) return kBadSeq;
+  if (child == nullptr) return kBadArg;
+  if (seqs_.size() >= static_cast<size_t>(INT32_MAX)) return kCapacity;
+  Seq c;
+  try {
+    c.table = seqs_[parent].table;
+    seqs_.reserve(seqs_.size() + 1);
+  } catch (const std::bad_alloc&) {
+    return kCapacity;
+  }
+  c.len = seqs_[parent].len;
+  c.live = true;
+  for (int32_t b : c.table) {
+    if (ref_[b] == 1) ++shared_;
+    ++ref_[b];
+    ++refs_;
+  }
+  tokens_ += c.len;
+  waste_ += static_cast<int64_t>(c.table.size()) * bs_ - c.len;
+  seqs_.push_back(std::move(c));
+  *child = static_cast<int32_t>(seqs_.size() - 1);
+  ++live_seqs_;
+  return kOk;
+}
+
+Status BlockPool::seq_free(int32_t seq) {
+  if (!live(seq)) return kBadSeq;
+  Seq& s = seqs_[seq];
+  for (int32_t b : s.table) {
+    if (ref_[b] == 2) --shared_;
+    --ref_[b];
+    --refs_;
+    if (ref_[b] == 0) push_back(b);
+  }
+  tokens_ -= s.len;
+  waste_ -= static_cast<int64_t>(s.table.size()) * bs_ - s.len;
+  std::vector<int32_t>().swap(s.table);
+  s.len = 0;
+  s.live = false;
+  --live_seqs_;
+  return kOk;
+}
+
+Status BlockPool::block_tables(const int32_t* seqs, int32_t n, int32_t max_blocks,
+                               int32_t* tables, int32_t* lens, std::string* err) const {
+  if (n < 0 || max_blocks < 0 || (n > 0 && (seqs == nullptr || tables == nullptr))) {
+    *err = "pa_block_tables: bad arguments";
+    return kBadArg;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (!live(seqs[i])) {
+      *err = "pa_block_tables: unknown sequence";
+      return kBadSeq;
+    }
+    if (seqs_[seqs[i]].table.size() > static_cast<size_t>(max_blocks)) {
+      *err = "pa_block_tables: a table is longer than max_blocks";
+      return kCapacity;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = seqs_[seqs[i]];
+    int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
+    const int32_t nb = static_cast<int32_t>(s.table.size());
+    for (int32_t j = 0; j < nb; ++j) row[j] = s.table[j];
+    for (int32_t j = nb; j < max_blocks; ++j) row[j] = -1;
+    if (lens) lens[i] = static_cast<int32_t>(s.len);
+  }
+  return kOk;
+}
+
+Status BlockPool::seq_table(int32_t seq, int32_t* table, int32_t cap, int32_t* n_out,
+                            int32_t* len_out) const {
+  if (!live(seq)) return kBadSeq;
+  const Seq& s = seqs_[seq];
+  const int32_t nb = static_cast<int32_t>(s.table.size());
+  if (n_out) *n_out = nb;
+  if (len_out) *len_out = static_cast<int32_t>(s.len);
+  if (table == nullptr) return kOk;
+  if (nb > cap) return kCapacity;
+  for (int32_t j = 0; j < nb; ++j) table[j] = s.table[j];
+  return kOk;
+}
+
+void BlockPool::state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) const {
+  if (st) {
+    st->num_blocks = n_;
+    st->free_blocks = nfree_;
+    st->used_blocks = n_ - nfree_;
+    st->shared_blocks = shared_;
+    st->total_refs = refs_;
+    st->cow_copies = cow_copies_;
+    st->live_seqs = live_seqs_;
+    st->tokens = tokens_;
+    st->waste_tokens = waste_;
+  }
+  if (free_order) {
+    int32_t i = 0;
+    for (int32_t b = head_; b >= 0; b = next_[b]) free_order[i++] = b;
+  }
+  if (ref_cnt) {
+    for (int32_t b = 0; b < n_; ++b) ref_cnt[b] = ref_[b];
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,79 @@
+// Host block manager for the paged KV cache.
+//
+// Model ([p2] "PagedAttention: KV cache as virtual memory", sections "Direct
+// answer" and "Deep dive"; [p3] "PagedAttention: Why Static Batching Wastes Your
+// KV Cache", sections on on-demand blocks and copy-on-write):
+//   * a pool of fixed-size physical blocks shared by every sequence;
+//   * a free queue, doubly linked through two int32 arrays, giving O(1) take
+//     from the front, return to the back and (for later prefix caching) removal
+//     from the middle;
+//   * a reference count per block; a block returns to the queue at zero;
+//   * per sequence: a block table (logical -> physical) and a token count.
+// Every mutating call is all-or-nothing: it validates and reserves host memory
+// first, and only then changes state.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace pa {
+
+enum Status : int32_t {
+  kOk = 0,
+  kNoBlocks = 1,
+  kBadSeq = 2,
+  kBadArg = 3,
+  kCapacity = 4,
+};
+
+struct PoolStats {
+  int64_t num_blocks, free_blocks, used_blocks, shared_blocks, total_refs, cow_copies,
+      live_seqs, tokens, waste_tokens;
+};
+
+class BlockPool {
+ public:
+  // order: nullptr for 0..n-1, else a permutation (validated by create()).
+  static Status create(int32_t num_blocks, int32_t block_size, const int32_t* order,
+                       BlockPool** out, std::string* err);
+
+  Status seq_create(int32_t* id);
+  // slots: n entries; cow: {src, dst} or {-1, -1}.
+  Status alloc_append(int32_t seq, int32_t n, int32_t* slots, int32_t* cow, std::string* err);
+  Status fork(int32_t parent, int32_t* child);
+  Status seq_free(int32_t seq);
+  Status block_tables(const int32_t* seqs, int32_t n, int32_t max_blocks, int32_t* tables,
+                      int32_t* lens, std::string* err) const;
+  Status seq_table(int32_t seq, int32_t* table, int32_t cap, int32_t* n_out,
+                   int32_t* len_out) const;
+  void state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) const;
+
+  int32_t num_blocks() const { return n_; }
+  int32_t block_size() const { return bs_; }
+
+ private:
+  BlockPool(int32_t n, int32_t bs);
+  bool live(int32_t seq) const {
+    return seq >= 0 && seq < static_cast<int32_t>(seqs_.size()) && seqs_[seq].live;
+  }
+  int32_t pop_front();
+  void push_back(int32_t b);
+
+  struct Seq {
+    std::vector<int32_t> table;
+    int64_t len = 0;
+    bool live = false;
+  };
+
+  int32_t n_, bs_;
+  // free queue: next_/prev_ links, -1 terminated; in_queue_ marks membership
+  std::vector<int32_t> next_, prev_;
+  std::vector<uint8_t> in_queue_;
+  int32_t head_ = -1, tail_ = -1, nfree_ = 0;
+  std::vector<int32_t> ref_;
+  std::vector<Seq> seqs_;  // indexed by id; ids are never reused
+  int64_t live_seqs_ = 0, tokens_ = 0, waste_ = 0, cow_copies_ = 0, shared_ = 0, refs_ = 0;
+};
+
+}  // namespace pa

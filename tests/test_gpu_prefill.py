@@ -1,0 +1,104 @@
+"""GPU parity of chunked prefill (pa_write_kv of prior context and chunk, then
+pa_prefill_chunk) against the float64 oracle; small cases element by element,
+the full 8 x 512-row batch on sampled rows."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_394_amd as pa
+import workloads
+from gpu_harness import close
+from oracle import attention_fp64
+
+pytestmark = pytest.mark.gpu
+
+
+class PrefillCase:
+    def __init__(self, w):
+        self.w = w
+        self.pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
+        self.cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim, fill=float("nan"))
+        self.ids = []
+        for b in range(w.batch):
+            s = pa.pa_seq_create(self.pool)
+            self.ids.append(s)
+            k, v = w.kv(b)
+            P, C = int(w.prior[b]), int(w.chunk[b])
+            for lo, n in ((0, P), (P, C)):      # prior context first, then the chunk
+                slots, _ = pa.pa_alloc_append(self.pool, s, n)
+                if n:
+                    pa.pa_write_kv(self.cache, torch.from_numpy(np.ascontiguousarray(k[lo:lo + n])).cuda(),
+                                   torch.from_numpy(np.ascontiguousarray(v[lo:lo + n])).cuda(),
+                                   torch.from_numpy(slots).cuda())
+        L = int(w.lens.max())
+        self.max_blocks = max(1, -(-L // 16))
+        tables, _ = pa.pa_block_tables(self.pool, self.ids, self.max_blocks)
+        self.tables = torch.from_numpy(tables).cuda()
+        cu = np.concatenate([[0], np.cumsum(w.chunk)]).astype(np.int32)
+        self.cu_np = cu
+        self.cu = torch.from_numpy(cu).cuda()
+        self.prior = torch.from_numpy(w.prior.astype(np.int32)).cuda()
+        self.q = torch.from_numpy(w.q).cuda()
+        self.out = torch.full((int(cu[-1]), w.num_heads, w.head_dim), float("nan"),
+                              dtype=torch.float32, device="cuda")
+
+    def run(self):
+        pa.pa_prefill_chunk(self.cache, self.q, self.cu, self.prior, self.tables,
+                            int(self.w.chunk.max()), self.w.scale, self.out)
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()
+
+    def ref_row(self, b, i, h):
+        w = self.w
+        k, v = w.kv(b, cache=True)
+        kh = h // (w.num_heads // w.num_kv_heads)
+        n = int(w.prior[b]) + i + 1
+        r = int(self.cu_np[b]) + i
+        return attention_fp64(w.q[r, h], k[:n, kh], v[:n, kh], w.scale)
+
+
+def check_all(case):
+    got = case.run()
+    w = case.w
+    for b in range(w.batch):
+        for i in range(int(w.chunk[b])):
+            r = int(case.cu_np[b]) + i
+            for h in range(w.num_heads):
+                close(got[r, h], case.ref_row(b, i, h))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_small_ragged_prefill(D):
+    # P = 0, chunks shorter / longer than the 128-row tile, prior not block aligned
+    w = workloads.custom_prefill(101 + D, [0, 37, 300, 16, 0], [1, 21, 200, 129, 64], 2, 2, D)
+    check_all(PrefillCase(w))
+
+
+def test_grouped_heads_prefill():
+    w = workloads.custom_prefill(111, [50, 3], [70, 130], 6, 2, 128)
+    check_all(PrefillCase(w))
+
+
+def test_single_row_chunk_equals_decode():
+    w = workloads.custom_prefill(121, [45, 0, 700], [1, 1, 1], 4, 4, 128)
+    case = PrefillCase(w)
+    got = case.run()
+    lens = torch.from_numpy((w.prior + 1).astype(np.int32)).cuda()
+    out = torch.empty((3, 4, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.pa_decode_workspace_bytes(3, 4, 128, 701), dtype=torch.uint8, device="cuda")
+    pa.pa_decode(case.cache, case.q.view(3, 4, 128), case.tables, lens, 701, w.scale, out, ws)
+    torch.cuda.synchronize()
+    close(got.reshape(3, 4, 128), out.cpu().numpy().astype(np.float64))
+
+
+def test_chunked_prefill_full_size_sampled():
+    w = workloads.chunked_prefill()
+    case = PrefillCase(w)
+    got = case.run()
+    assert np.isfinite(got).all()
+    rows = [0, 1, 63, 64, 127, 128, 255, 256, 383, 400, 511]
+    for b in range(w.batch):
+        for i in rows:
+            for h in (0, 21, 39):
+                close(got[int(case.cu_np[b]) + i, h], case.ref_row(b, i, h))

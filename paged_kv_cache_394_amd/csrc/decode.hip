@@ -66,9 +66,13 @@ struct QReg<false> {
     for (int j = 0; j < 4; ++j) v[j] = half2_t{x[2 * j], x[2 * j + 1]};
   }
   __device__ float dot(const u32x4_t& k) const {
+    // bit-cast the whole vector: a bit_cast of one element expression (k[j])
+    // is compiled as a read of element 0
+    const half8_t kh = __builtin_bit_cast(half8_t, k);
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k[j]), v[j], s, false);
+    for (int j = 0; j < 4; ++j)
+      s = __builtin_amdgcn_fdot2(half2_t{kh[2 * j], kh[2 * j + 1]}, v[j], s, false);
     return s;
   }
 };

@@ -95,7 +95,7 @@ _SIGNATURES = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; build it with `python -m paged_kv_cache_394_amd.build` "
+            f"{LIB_PATH} is not built; build it with `python paged_kv_cache_394_amd/build.py` (or __graft_entry__.build()) "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():

@@ -1,7 +1,8 @@
 """Build libpa.so in-tree with hipcc for gfx950.
 
 Every source under csrc/ is compiled (device code for gfx950 only) and linked
-into ``paged_kv_cache_394_amd/libpa.so``.  Run ``python -m paged_kv_cache_394_amd.build``.
+into ``paged_kv_cache_394_amd/libpa.so``.  Run ``python paged_kv_cache_394_amd/build.py``
+(this file imports nothing from the package, so it runs before the library exists).
 """
 
 from __future__ import annotations

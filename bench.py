@@ -3,24 +3,34 @@
 Step (timed): one decode iteration of the Llama-2-13B-shaped batch -- 64
 sequences, context lengths uniform in [1, 2048], 40 heads of 128, fp16 K/V in
 16-token blocks scattered over the pool.  The step writes the 64 new tokens'
-K/V into their slots (pa_write_kv) and runs the split-K paged decode
-(pa_decode: partition kernel + partition-reduce kernel).  The block-manager
-work of the iteration (allocation, table export) is host work, done before the
-timed region and timed on its own.
+K/V into their slots (pa_write_kv) and runs the paged decode (pa_decode).  The
+block-manager work of the iteration (allocation, table export) is host work,
+done before the timed region and timed on its own.
 
 Reported on one JSON line:
   value        KV-read GB/s of the step: algorithmic K+V bytes / step time
-  roofline     pa_decode (partition + reduce) against 8 TB/s, from HIP events
+  roofline     pa_decode against 8 TB/s, from HIP events on its stream
+  ceiling      a plain device copy of 1 GiB (read + write GB/s), for context
   fp8_decode   the same batch with an e4m3 cache
+  prefix_cow   32 sequences sharing an 800-token prompt: GB/s on unique and on
+               logical K/V bytes
   prefill      chunked prefill, 8 x 512-token chunks over 0..4096 cached tokens,
                causal-valid FLOPs / time against the 2.5 PFLOP/s fp16 MFMA peak
   host         block-manager call rates
   cpu_baseline the float64 oracle on a bounded sample of the batch (host cores)
+
+Counter runs: ``--pmc-run`` does only a 256 MiB device copy (torch.neg, one
+elementwise kernel that reads and writes 256 MiB) and a few decode steps, for
+``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE``; ``--summarize-pmc FETCH_DIR
+WRITE_DIR`` turns the two counter CSVs into profiles/decode_llama13b_fp16_traffic.md,
+scaling the decode kernel's counts by the copy's (known bytes / counted bytes).
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -31,9 +41,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 METRIC = "paged decode KV-read GB/s and % of HBM peak; tokens/s; prefill MFMA util"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama13b_fp16_traffic.md")
+PMC_COPY_BYTES = 256 << 20
+PMC_DECODE_STEPS = 5
 
 
 def log(msg):
@@ -49,36 +62,36 @@ def kernel_source_hash() -> str:
 
 
 def read_traffic():
-    """HBM bytes per pa_decode launch from the committed rocprofv3 counter
+    """HBM bytes (read, written) per pa_decode launch from the committed counter
     summary, if it was taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "decode_llama13b_fp16_traffic.md")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    text = open(path).read()
+    text = open(TRAFFIC_FILE).read()
     m_src = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
-    m_val = re.search(r"HBM bytes per pa_decode call: `([0-9.eE+]+)`", text)
-    if not m_src or not m_val or m_src.group(1) != kernel_source_hash():
+    m_rd = re.search(r"HBM bytes read per pa_decode call: `([0-9.eE+]+)`", text)
+    m_wr = re.search(r"HBM bytes written per pa_decode call: `([0-9.eE+]+)`", text)
+    if not (m_src and m_rd and m_wr) or m_src.group(1) != kernel_source_hash():
         return None
-    return float(m_val.group(1))
+    return float(m_rd.group(1)), float(m_wr.group(1))
+
+
+def fp8_scales(w, np):
+    ka = va = np.float32(0)
+    for b in range(w.batch):
+        k, v = w.kv(b)
+        ka = max(ka, np.abs(k.astype(np.float32)).max())
+        va = max(va, np.abs(v.astype(np.float32)).max())
+    return float(np.float32(ka / np.float32(448))), float(np.float32(va / np.float32(448)))
 
 
 def setup_decode(w, fp8: bool, pa, torch, np):
     """Admit every sequence with its context minus the newest token, write that
     KV, then allocate the newest token (the step's write target)."""
     pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
-    if fp8:
-        ka = va = np.float32(0)
-        for b in range(w.batch):
-            k, v = w.kv(b)
-            ka = max(ka, np.abs(k.astype(np.float32)).max())
-            va = max(va, np.abs(v.astype(np.float32)).max())
-        ks, vs = float(np.float32(ka / np.float32(448))), float(np.float32(va / np.float32(448)))
-    else:
-        ks = vs = 1.0
+    ks, vs = fp8_scales(w, np) if fp8 else (1.0, 1.0)
     cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim, fp8=fp8, k_scale=ks, v_scale=vs)
     ids, new_k, new_v, new_slots = [], [], [], []
     t_alloc = 0.0
-    n_alloc = 0
     for b in range(w.batch):
         s = pa.pa_seq_create(pool)
         ids.append(s)
@@ -87,7 +100,6 @@ def setup_decode(w, fp8: bool, pa, torch, np):
         t0 = time.perf_counter()
         slots, _ = pa.pa_alloc_append(pool, s, L - 1)
         t_alloc += time.perf_counter() - t0
-        n_alloc += 1
         if L > 1:
             pa.pa_write_kv(cache, torch.from_numpy(k[:L - 1]).cuda(), torch.from_numpy(v[:L - 1]).cuda(),
                            torch.from_numpy(slots).cuda())
@@ -95,7 +107,7 @@ def setup_decode(w, fp8: bool, pa, torch, np):
         new_v.append(v[L - 1:])
     t0 = time.perf_counter()
     for s in ids:
-        slots, cow = pa.pa_alloc_append(pool, s, 1)
+        slots, _ = pa.pa_alloc_append(pool, s, 1)
         new_slots.append(int(slots[0]))
     t_step_alloc = time.perf_counter() - t0
     max_ctx = int(w.lens.max())
@@ -112,22 +124,26 @@ def setup_decode(w, fp8: bool, pa, torch, np):
         "tables": torch.from_numpy(tables).cuda(), "lens": torch.from_numpy(lens).cuda(),
         "q": torch.from_numpy(w.q).cuda(), "max_ctx": max_ctx,
         "out": torch.empty((w.batch, w.num_heads, w.head_dim), dtype=torch.float32, device="cuda"),
-        "host": {"admit_us_per_seq": 1e6 * t_alloc / n_alloc,
-                 "append1_us_per_seq": 1e6 * t_step_alloc / len(ids),
-                 "table_export_us": 1e6 * t_export},
+        "host": {"admit_us_per_seq": round(1e6 * t_alloc / w.batch, 3),
+                 "append1_us_per_seq": round(1e6 * t_step_alloc / len(ids), 3),
+                 "table_export_us": round(1e6 * t_export, 3)},
     }
     nbytes = pa.pa_decode_workspace_bytes(w.batch, w.num_heads, w.head_dim, max_ctx)
-    d["ws"] = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d["ws"] = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     return d
 
 
+def decode_call(pa, w, d):
+    pa.pa_decode(d["cache"], d["q"], d["tables"], d["lens"], d["max_ctx"], w.scale, d["out"], d["ws"])
+
+
 def run_decode(pa, torch, w, d, steps, warmup):
-    """Returns (ms per step, ms per pa_decode from events)."""
+    """Returns (ms per step, mean and median ms per pa_decode from events)."""
     def step(ev=None):
         pa.pa_write_kv(d["cache"], d["k_new"], d["v_new"], d["slots"])
         if ev is not None:
             ev[0].record()
-        pa.pa_decode(d["cache"], d["q"], d["tables"], d["lens"], d["max_ctx"], w.scale, d["out"], d["ws"])
+        decode_call(pa, w, d)
         if ev is not None:
             ev[1].record()
 
@@ -145,13 +161,77 @@ def run_decode(pa, torch, w, d, steps, warmup):
     return 1e3 * (t1 - t0) / steps, mean_dec, dec_ms[len(dec_ms) // 2]
 
 
-def decode_bytes(w, elem_bytes):
+def decode_bytes(w, elem_bytes, lens=None):
     """Algorithmic bytes of one pa_decode: K and V rows of every cached token
-    read once, q read, fp32 output written (partials are implementation detail)."""
-    kv = int(w.lens.sum()) * w.num_kv_heads * w.head_dim * 2 * elem_bytes
+    read once, q read, fp32 output written, block tables and lengths read
+    (split partials, when used, are not algorithmic)."""
+    lens = w.lens if lens is None else lens
+    kv = int(lens.sum()) * w.num_kv_heads * w.head_dim * 2 * elem_bytes
     io = w.batch * w.num_heads * w.head_dim * (2 + 4)
-    tables = w.batch * (-(-int(w.lens.max()) // 16)) * 4
+    tables = w.batch * (-(-int(lens.max()) // 16)) * 4 + w.batch * 4
     return kv, kv + io + tables
+
+
+def time_events(torch, fn, reps, warmup=3):
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def copy_ceiling(torch, nbytes=1 << 30, reps=20):
+    """A plain device copy (one elementwise kernel) as the bandwidth context."""
+    src = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    mean, _ = time_events(torch, lambda: torch.neg(src, out=dst), reps)
+    del src, dst
+    return {"kind": "torch.neg over 1 GiB fp16 (read 1 GiB + write 1 GiB)",
+            "gbs_read_plus_write": round(2 * nbytes / (mean * 1e-3) / 1e9, 1), "ms": round(mean, 4)}
+
+
+def bench_prefix(pa, torch, np, workloads, reps):
+    """32 sequences fork one 800-token prompt and append private tails; one
+    decode query each.  The prompt's blocks are stored once and read by every
+    sequence."""
+    w = workloads.prefix_cow()
+    pool = pa.pa_pool_create(w.num_blocks, 16)
+    cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim)
+    pk, pv = w.prompt_kv()
+    root = pa.pa_seq_create(pool)
+    slots, _ = pa.pa_alloc_append(pool, root, w.prompt_len)
+    pa.pa_write_kv(cache, torch.from_numpy(pk).cuda(), torch.from_numpy(pv).cuda(), torch.from_numpy(slots).cuda())
+    seqs = [root] + [pa.pa_fork_cow(pool, root) for _ in range(w.batch - 1)]
+    for b, s in enumerate(seqs):
+        k, v = w.kv(b)
+        slots, cow = pa.pa_alloc_append(pool, s, int(w.tails[b]))
+        pa.pa_write_kv(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                       torch.from_numpy(slots).cuda(), [cow] if cow else None)
+    max_ctx = int(w.lens.max())
+    tables, lens = pa.pa_block_tables(pool, seqs, -(-max_ctx // 16))
+    stats, _, _ = pa.pa_pool_state(pool)
+    d = {"cache": cache, "q": torch.from_numpy(w.q).cuda(), "tables": torch.from_numpy(tables).cuda(),
+         "lens": torch.from_numpy(lens).cuda(), "max_ctx": max_ctx,
+         "out": torch.empty((w.batch, w.num_heads, w.head_dim), dtype=torch.float32, device="cuda"),
+         "ws": torch.empty(max(16, pa.pa_decode_workspace_bytes(w.batch, w.num_heads, w.head_dim, max_ctx)),
+                           dtype=torch.uint8, device="cuda")}
+    mean, med = time_events(torch, lambda: decode_call(pa, w, d), reps)
+    per_tok = w.num_kv_heads * w.head_dim * 2 * 2
+    logical = int(w.lens.sum()) * per_tok
+    unique = (w.prompt_len + int(w.tails.sum())) * per_tok
+    return {"workload": "prefix_cow: 32 seqs share an 800-token prompt (50 blocks, ref_cnt 32), "
+                        "tails U[1,1024], 40 heads x 128, fp16",
+            "pa_decode_ms": round(mean, 5), "ms_median": round(med, 5),
+            "unique_kv_bytes": unique, "logical_kv_bytes": logical,
+            "unique_gbs": round(unique / (mean * 1e-3) / 1e9, 2),
+            "logical_gbs": round(logical / (mean * 1e-3) / 1e9, 2),
+            "used_blocks": stats["used_blocks"], "shared_blocks": stats["shared_blocks"]}
 
 
 def bench_prefill(pa, torch, np, workloads, reps):
@@ -177,27 +257,14 @@ def bench_prefill(pa, torch, np, workloads, reps):
     prior = torch.from_numpy(w.prior.astype(np.int32)).cuda()
     q = torch.from_numpy(w.q).cuda()
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-
-    def call():
-        pa.pa_prefill_chunk(cache, q, cu, prior, tables, int(w.chunk.max()), w.scale, out)
-
-    for _ in range(3):
-        call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        call()
-        b.record()
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
-    mean = sum(ms) / len(ms)
+    mean, med = time_events(
+        torch, lambda: pa.pa_prefill_chunk(cache, q, cu, prior, tables, int(w.chunk.max()), w.scale, out), reps)
     C = w.chunk.astype(np.float64)
     P = w.prior.astype(np.float64)
     flops = 4.0 * w.head_dim * w.num_heads * float(np.sum(C * P + C * (C + 1) / 2))
     tflops = flops / (mean * 1e-3) / 1e12
     return {"workload": "chunked_prefill: 8 seqs, prior U[0,4096], chunk 512, 40 heads x 128, fp16",
-            "ms": round(mean, 4), "ms_median": round(ms[len(ms) // 2], 4),
+            "ms": round(mean, 4), "ms_median": round(med, 4),
             "causal_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
             "mfma_util": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
             "peak_tflops": MFMA_F16_PEAK_TFLOPS}
@@ -215,19 +282,16 @@ def cpu_baseline(w, np, target_s=15.0):
         done_bytes = 0
         done_seqs = 0
         tokens = 0
-        outs = {}
         for b in range(w.batch):
             k, v = w.kv(b)
             L = int(w.lens[b])
-            t0 = time.perf_counter()
             nblk = -(-L // 16)
             pool = OraclePool(nblk, 16)
             cache = OracleCache(nblk, w.num_kv_heads, w.head_dim)
             _, s = pool.seq_create()
             _, slots, _ = pool.alloc_append(s, L)
             cache.write(slots, k, v)
-            o = paged_decode(cache, [pool.table(s)], [L], w.q[b:b + 1], w.scale)
-            outs[b] = o[0]
+            paged_decode(cache, [pool.table(s)], [L], w.q[b:b + 1], w.scale)
             done_bytes += L * w.num_kv_heads * w.head_dim * 2 * 2
             tokens += L
             done_seqs += 1
@@ -238,7 +302,87 @@ def cpu_baseline(w, np, target_s=15.0):
             "kind": "oracle",
             "sample": f"first {done_seqs} of {w.batch} sequences ({tokens} tokens, all 40 heads), "
                       f"{elapsed:.1f} s, float64 numpy, BLAS limited to 1 thread",
-            "seconds": round(elapsed, 2)}, outs
+            "seconds": round(elapsed, 2)}
+
+
+def pmc_run(pa, torch, np, workloads):
+    """Only what the counter runs need: one copy of known size, then a few decode
+    steps of the 13B-shaped batch."""
+    src = torch.ones(PMC_COPY_BYTES // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    w = workloads.llama13b_decode()
+    d = setup_decode(w, False, pa, torch, np)
+    for _ in range(PMC_DECODE_STEPS):
+        decode_call(pa, w, d)
+    torch.cuda.synchronize()
+    log(f"pmc run done: copy {PMC_COPY_BYTES} B, {PMC_DECODE_STEPS} decode calls")
+
+
+def _read_counter_csv(path, counter):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 CSV."""
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Write the traffic summary from two rocprofv3 --pmc runs of --pmc-run."""
+    def find(d):
+        hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not hits:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        return hits[0]
+
+    fetch = _read_counter_csv(find(fetch_dir), "FETCH_SIZE")
+    write = _read_counter_csv(find(write_dir), "WRITE_SIZE")
+
+    def pick(table, key):
+        names = [n for n in table if key in n]
+        if not names:
+            raise SystemExit(f"no kernel matching {key!r} in {sorted(table)}")
+        return names[0], table[names[0]]
+
+    copy_name, copy_f = pick(fetch, "neg")
+    _, copy_w = pick(write, "neg")
+    dec_name, dec_f = pick(fetch, "decode_")
+    _, dec_w = pick(write, "decode_")
+    known_kib = PMC_COPY_BYTES / 1024.0
+    f_scale = known_kib / copy_f[0]
+    w_scale = known_kib / copy_w[0]
+    dec_kernels = [n for n in fetch if "decode_" in n]
+    per_call_f = sum(sum(fetch[n]) for n in dec_kernels) / PMC_DECODE_STEPS
+    per_call_w = sum(sum(write.get(n, [0.0])) for n in dec_kernels) / PMC_DECODE_STEPS
+    rd = per_call_f * f_scale * 1024.0
+    wr = per_call_w * w_scale * 1024.0
+    text = f"""# pa_decode HBM traffic, llama13b_decode (64 seqs, L ~ U[1,2048], 40 x 128, fp16)
+
+Commands (from the repository root, on the GPU box):
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- python bench.py --pmc-run
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- python bench.py --pmc-run
+    python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write
+
+Calibration: `{copy_name[:60]}` copies {PMC_COPY_BYTES} B; FETCH_SIZE read {copy_f[0]:.1f} KiB
+(scale {f_scale:.4f}), WRITE_SIZE {copy_w[0]:.1f} KiB (scale {w_scale:.4f}).
+
+Decode kernels counted: {", ".join(sorted(set(n[:70] for n in dec_kernels)))}
+FETCH_SIZE per call (raw): {per_call_f:.1f} KiB; WRITE_SIZE per call (raw): {per_call_w:.1f} KiB
+
+- kernel source hash: `{kernel_source_hash()}`
+- HBM bytes read per pa_decode call: `{rd:.6e}`
+- HBM bytes written per pa_decode call: `{wr:.6e}`
+"""
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text)
 
 
 def main():
@@ -249,10 +393,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="decode step only (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pmc-run", action="store_true", help="copy + decode only, for counter runs")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU "
-              f"path (asked for --gpus {args.gpus})", file=sys.stderr)
+        print(f"bench.py measures one GPU: this library runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -262,6 +411,9 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.pmc_run:
+        pmc_run(pa, torch, np, workloads)
+        return
     log("generating the 13B-shaped decode batch")
     w = workloads.llama13b_decode()
     d = setup_decode(w, False, pa, torch, np)
@@ -291,10 +443,12 @@ def main():
                    "kv_bytes_per_step": kv_bytes},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
-        "roofline": {"kernel": "pa_decode (decode_partition + decode_reduce)", "bound": "hbm",
+        "roofline": {"kernel": "pa_decode (decode_seq_kernel)", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else round(traffic, 0),
+                     "traffic": None if traffic is None else round(traffic[0] + traffic[1], 0),
+                     "traffic_read": None if traffic is None else round(traffic[0], 0),
+                     "traffic_write": None if traffic is None else round(traffic[1], 0),
                      "algorithmic_bytes": alg_bytes, "ms_mean": round(dec_ms, 5),
                      "ms_median": round(dec_med, 5)},
         "host": d["host"],
@@ -302,6 +456,8 @@ def main():
     del d
     torch.cuda.empty_cache()
     if not args.no_extras:
+        log("copy ceiling")
+        res["ceiling"] = copy_ceiling(torch)
         log("decode e4m3")
         d8 = setup_decode(w, True, pa, torch, np)
         ms8, dec8, _ = run_decode(pa, torch, w, d8, args.steps, args.warmup)
@@ -312,12 +468,14 @@ def main():
                              "hbm_frac": round(alg8 / (dec8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del d8
         torch.cuda.empty_cache()
+        log("prefix sharing decode")
+        res["prefix_cow"] = bench_prefix(pa, torch, np, workloads, args.steps)
+        torch.cuda.empty_cache()
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cb, outs = cpu_baseline(w, np, args.cpu_seconds)
-        res["cpu_baseline"] = cb
+        res["cpu_baseline"] = cpu_baseline(w, np, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

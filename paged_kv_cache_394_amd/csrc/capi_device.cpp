@@ -102,6 +102,8 @@ pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
   if (!aligned16(q) || !aligned16(out_dev)) return fail(PA_ERR_BAD_ARG, "pa_decode: q / out must be 16-byte aligned");
   if (num_heads > 65535 || B > 65535) return fail(PA_ERR_BAD_ARG, "pa_decode: num_heads and B must be <= 65535");
   if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, "pa_decode: scale must be finite");
+  if (pa::decode_units(B, num_heads, max_context_len) > (int64_t(1) << 31) - 64)
+    return fail(PA_ERR_BAD_ARG, "pa_decode: B * num_heads * ceil(max_context_len / 256) too large for one launch");
   const size_t need = pa::decode_workspace_bytes(B, num_heads, d.head_dim, max_context_len);
   if (workspace_bytes < need || (need > 0 && workspace_dev == nullptr))
     return fail(PA_ERR_BAD_ARG, "pa_decode: workspace smaller than pa_decode_workspace_bytes()");

@@ -24,9 +24,11 @@ hipError_t launch_copy_blocks(const KvDesc& c, const int32_t* pairs, int32_t n, 
 hipError_t launch_write_kv(const KvDesc& c, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t T, hipStream_t s);
 
-// Split-K decode: partition kernel + partition reduce.
+// Split-K decode: split kernel + split reduce.
 int32_t decode_partition_tokens();
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len);
+// Work units (one wave each) of one decode launch; must stay below 2^31.
+int64_t decode_units(int32_t B, int32_t Hq, int32_t max_context_len);
 hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                          const int32_t* lens, int32_t B, int32_t max_blocks, int32_t max_context_len,
                          float scale, float* out, void* workspace, hipStream_t s);

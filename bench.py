@@ -394,6 +394,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="decode step only (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--pmc-run", action="store_true", help="copy + decode only, for counter runs")
+    ap.add_argument("--prefill-only", action="store_true", help="the chunked-prefill leg only (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -413,6 +414,9 @@ def main():
     torch.cuda.set_device(0)
     if args.pmc_run:
         pmc_run(pa, torch, np, workloads)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(pa, torch, np, workloads, 20)}), flush=True)
         return
     log("generating the 13B-shaped decode batch")
     w = workloads.llama13b_decode()

@@ -21,6 +21,20 @@
 // same permutation.  Online softmax in the log2 domain, fp32 statistics, P
 // rounded to fp16 for the MFMA, fp32 accumulation.  The causal mask is applied
 // only on tiles that cross the diagonal.
+//
+// Staging.  The K/V tiles are double-buffered in LDS: the global loads of tile
+// t+1 are issued into registers before tile t is computed and written to the
+// other buffer after it, so one barrier per tile separates the phases.  The
+// tile's 4 block ids are read with scalar loads, so every address is a scalar
+// block base plus a per-thread constant.  V is transposed in registers on the
+// way: a thread loads 8 keys x 4 columns (8-byte loads) and writes 4 rows of
+// V^T, in a key order that makes each MFMA operand one 16-byte LDS read.
+//
+// Order.  Workgroups are dispatched longest sequence first (prior + chunk;
+// every workgroup ranks the <= 64 sequences itself), and the query tiles of one
+// (sequence, head) are given workgroup ids 8 apart, which the dispatcher sends
+// to the same XCD: they read the same K/V tiles at about the same time and
+// share that XCD's L2.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -34,31 +48,184 @@ using namespace dev;
 constexpr int kBq = 128;       // query rows per workgroup
 constexpr int kBk = 64;        // keys per tile
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;       // workgroup ids are dealt round robin over 8 XCDs
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+struct PGeom {
+  static constexpr int KP = D + 8;          // LDS row stride of K (halfs)
+  // LDS row stride of V^T (halfs).  Within each 32-key pair of a V^T row,
+  // key 16 hb + 4 g + i (hb < 2, g < 4, i < 4) is stored at 8 g + 4 hb + i, so
+  // the 8 keys lane group g feeds to one P.V MFMA are one 16-byte run.
+  static constexpr int VP = kBk + 8;
+  static constexpr int DK = D / 32;         // MFMA steps over head_dim for S
+  static constexpr int DT = D / 16;         // 16-wide output tiles over head_dim
+  static constexpr int CPR = D / 8;         // 16-byte chunks per K row
+  static constexpr int KLOADS = kBk * CPR / kThreads;        // K chunks per thread
+  static constexpr int VCOMBOS = (kBk / 8) * (D / 4);          // (8 keys x 4 columns) groups
+  static constexpr int VLOADS = (VCOMBOS + kThreads - 1) / kThreads;
+  static constexpr int KBUF = kBk * KP;     // halfs per K buffer
+  static constexpr int VBUF = D * VP;       // halfs per V^T buffer
+  static_assert(kBk * CPR % kThreads == 0, "K tile must split evenly");
+};
+
+// Registers holding one K/V tile between its global loads and its LDS stores.
+template <int D>
+struct Stage {
+  u32x4_t k[PGeom<D>::KLOADS];
+  u32x2_t v[PGeom<D>::VLOADS][8];
+};
+
+// Rank of lane b's sequence (b < B <= 64) by total length, longest first,
+// ties by index; lanes >= B get rank 64.
+__device__ __forceinline__ int work_rank(int Wb, int lane, int B) {
+  int rank = 0;
+  for (int k = 0; k < B; ++k) {
+    const int Wk = __builtin_amdgcn_readlane(Wb, k);
+    rank += (Wk > Wb || (Wk == Wb && k < lane)) ? 1 : 0;
+  }
+  return lane < B ? rank : 64;
+}
+
+// The 4 block ids of key tile kt (wave-uniform scalar loads; ids past the
+// table's end, or outside the pool, read as block 0), as four scalars.
+struct TileBlocks {
+  int p0, p1, p2, p3;
+};
+
+// Block j (0..3, may differ per lane) of a tile.  A free function on values:
+// as a member reading this->pN the selects are folded into one indexed load
+// and the struct is left in memory.
+__device__ __forceinline__ int pick_block(int j, int p0, int p1, int p2, int p3) {
+  const int lo = (j & 1) ? p1 : p0;
+  const int hi = (j & 1) ? p3 : p2;
+  return (j & 2) ? hi : lo;
+}
+
+__device__ __forceinline__ int table_id(const int32_t* __restrict__ trow, int idx, int max_blocks,
+                                        int num_blocks) {
+  int v = idx < max_blocks ? trow[idx] : 0;
+  v = __builtin_amdgcn_readfirstlane(v);
+  return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
+}
+
+__device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ trow, int kt,
+                                                  int max_blocks, int num_blocks) {
+  const int j0 = kt * (kBk / kBlock);
+  return TileBlocks{table_id(trow, j0, max_blocks, num_blocks),
+                    table_id(trow, j0 + 1, max_blocks, num_blocks),
+                    table_id(trow, j0 + 2, max_blocks, num_blocks),
+                    table_id(trow, j0 + 3, max_blocks, num_blocks)};
+}
+
+// Issue the global loads of key tile key0 .. key0 + kBk - 1 (keys at or past
+// n_keys load zeros).  blk_stride: halfs per physical block of one cache.
+// K load i of thread t is 16-byte chunk i * 256 + t of the tile, i.e. key
+// (i * 256 + t) / CPR, in the tile's block i * 256 / (16 CPR) + t / (16 CPR)
+// (the first term is a constant); the thread's V group is 8 consecutive keys
+// of one block and 4 columns.
+template <int D>
+__device__ __forceinline__ void load_tile(Stage<D>& st, const TileBlocks& tb,
+                                          const half_t* __restrict__ kc,
+                                          const half_t* __restrict__ vc, int64_t blk_stride,
+                                          int kvh, int key0, int n_keys, int tid) {
+  using G = PGeom<D>;
+#pragma unroll
+  for (int i = 0; i < G::KLOADS; ++i) {
+    const int cidx = i * kThreads + tid;
+    const int key = cidx / G::CPR;
+    const int blk = (i * kThreads) / (kBlock * G::CPR) + tid / (kBlock * G::CPR);
+    const int off = ((kvh * kBlock + (key & 15)) * D) + (cidx % G::CPR) * 8;
+    st.k[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (key0 + key < n_keys)
+      st.k[i] = *reinterpret_cast<const u32x4_t*>(kc + static_cast<int64_t>(pick_block(blk, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride + off);
+  }
+#pragma unroll
+  for (int i = 0; i < G::VLOADS; ++i) {
+    const int combo = i * kThreads + tid;
+    const int kg = combo % (kBk / 8);
+    const int dq = combo / (kBk / 8);
+    const int off = (kvh * kBlock + 8 * (kg & 1)) * D + 4 * dq;
+    const half_t* src = vc + static_cast<int64_t>(pick_block(kg >> 1, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride + off;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      st.v[i][r] = u32x2_t{0u, 0u};
+      if (combo < G::VCOMBOS && key0 + 8 * kg + r < n_keys)
+        st.v[i][r] = *reinterpret_cast<const u32x2_t*>(src + r * D);
+    }
+  }
+}
+
+// Write a staged tile to one LDS buffer: K row-major, V transposed.
+template <int D>
+__device__ __forceinline__ void store_tile(const Stage<D>& st, half_t* __restrict__ sK,
+                                           half_t* __restrict__ sVt, int tid) {
+  using G = PGeom<D>;
+#pragma unroll
+  for (int i = 0; i < G::KLOADS; ++i) {
+    const int cidx = i * kThreads + tid;
+    const int key = cidx / G::CPR;
+    const int d0 = (cidx % G::CPR) * 8;
+    *reinterpret_cast<u32x4_t*>(&sK[key * G::KP + d0]) = st.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < G::VLOADS; ++i) {
+    const int combo = i * kThreads + tid;
+    if (combo >= G::VCOMBOS) continue;
+    const int kg = combo % (kBk / 8);
+    const int dq = combo / (kBk / 8);
+    // row j of the 4 columns: halves j of the 8 keys, packed two keys a word
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t row;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a = st.v[i][2 * w][j >> 1];
+        const uint32_t b = st.v[i][2 * w + 1][j >> 1];
+        row[w] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      // keys 8 kg .. 8 kg + 7 of the permuted row (see PGeom): two runs of 4
+      const int base = (4 * dq + j) * G::VP + (kg >> 2) * 32 + 16 * (kg & 1) + 4 * ((kg >> 1) & 1);
+      *reinterpret_cast<u32x2_t*>(&sVt[base]) = u32x2_t{row[0], row[1]};
+      *reinterpret_cast<u32x2_t*>(&sVt[base + 8]) = u32x2_t{row[2], row[3]};
+    }
+  }
+}
+
+// grid (ceil(B * Hq / 8) * 8 * nqt), block 256.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
-    const int32_t* __restrict__ tables, float* __restrict__ out, int32_t Hq, int32_t Hkv,
-    int32_t total_q, int32_t max_blocks, int32_t num_blocks, float qk_scale) {
-  constexpr int KP = D + 8;     // LDS row stride of K (halfs)
-  constexpr int VP = kBk + 8;   // LDS row stride of V^T (halfs)
-  constexpr int DK = D / 32;    // MFMA steps over head_dim for S
-  constexpr int DT = D / 16;    // 16-wide output tiles over head_dim
-  constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
-  constexpr int CHUNKS = kBk * CPR;
-  static_assert(CHUNKS % kThreads == 0, "tile load must split evenly");
-  __shared__ __attribute__((aligned(16))) half_t sK[kBk * KP];
-  __shared__ __attribute__((aligned(16))) half_t sVt[D * VP];
+    const int32_t* __restrict__ tables, float* __restrict__ out, int32_t B, int32_t Hq,
+    int32_t Hkv, int32_t total_q, int32_t max_blocks, int32_t num_blocks, int32_t nqt,
+    float qk_scale) {
+  using G = PGeom<D>;
+  __shared__ __attribute__((aligned(16))) half_t sK[2 * G::KBUF];
+  __shared__ __attribute__((aligned(16))) half_t sVt[2 * G::VBUF];
 
-  const int qt = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int g = lane >> 4;
   const int c16 = lane & 15;
+
+  // workgroup -> (query tile, pair): ids 8 apart share a pair, so one XCD
+  const int u = blockIdx.x;
+  const int x = u % kXcds;
+  const int rest = u / kXcds;
+  const int qt = rest % nqt;
+  const int pair = (rest / nqt) * kXcds + x;
+  if (pair >= B * Hq) return;
+  const int h = pair % Hq;
+  const int rank = pair / Hq;
+  int b;
+  if (B <= 64) {
+    int Wb = 0;
+    if (lane < B) Wb = max(prior[lane], 0) + (cu_q[lane + 1] - cu_q[lane]);
+    b = __ffsll(static_cast<unsigned long long>(__ballot(work_rank(Wb, lane, B) == rank))) - 1;
+  } else {
+    b = rank;
+  }
 
   const int row0 = cu_q[b];
   const int C = cu_q[b + 1] - row0;
@@ -70,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
 
   // Q as the B operand of S^T = K Q^T: lane holds q[row = c16][d = 32 kk + 8 g .. +8]
-  half8_t qb[2][DK];
+  half8_t qb[2][G::DK];
   int qrow[2];
   bool qvalid[2];
 #pragma unroll
@@ -79,19 +246,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     qvalid[st] = qrow[st] < C && (row0 + qrow[st]) < total_q;
     const half_t* qp = q + (static_cast<int64_t>(row0 + qrow[st]) * Hq + h) * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
+    for (int kk = 0; kk < G::DK; ++kk) {
       qb[st][kk] = qvalid[st] ? *reinterpret_cast<const half8_t*>(qp + 32 * kk) : half8_t{};
     }
   }
 
-  float4_t o[2][DT];
+  float4_t o[2][G::DT];
   float m[2], l[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     m[st] = -INFINITY;
     l[st] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[st][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < G::DT; ++dt) o[st][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   const int wq_first = q0 + 32 * w;                      // first query row of this wave
@@ -99,109 +266,104 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int n_keys = min(P + min(q0 + kBq, C), L_total);  // keys any row of the group needs
   const int ntiles = (n_keys + kBk - 1) / kBk;
 
+  const int64_t blk_stride = static_cast<int64_t>(Hkv) * kBlock * D;
+  Stage<D> stg;
+  if (ntiles > 0) {
+    load_tile<D>(stg, tile_blocks(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, kvh, 0,
+                 n_keys, tid);
+    store_tile<D>(stg, sK, sVt, tid);
+  }
+
   for (int kt = 0; kt < ntiles; ++kt) {
     const int key0 = kt * kBk;
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int pass = 0; pass < CHUNKS / kThreads; ++pass) {
-      const int cidx = pass * kThreads + tid;
-      const int key = cidx / CPR;        // key within the tile
-      const int d0 = (cidx % CPR) * 8;
-      const int kabs = key0 + key;
-      u32x4_t kv = u32x4_t{0u, 0u, 0u, 0u};
-      u32x4_t vv = u32x4_t{0u, 0u, 0u, 0u};
-      if (kabs < L_total) {
-        int phys = trow[kabs >> 4];
-        phys = (static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks)) ? phys : 0;
-        const int64_t off =
-            ((static_cast<int64_t>(phys) * Hkv + kvh) * kBlock + (kabs & 15)) * D + d0;
-        kv = *reinterpret_cast<const u32x4_t*>(kc + off);
-        vv = *reinterpret_cast<const u32x4_t*>(vc + off);
-      }
-      *reinterpret_cast<u32x4_t*>(&sK[key * KP + d0]) = kv;
-      const half8_t vh = __builtin_bit_cast(half8_t, vv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(d0 + e) * VP + key] = vh[e];
-    }
-    __syncthreads();
+    const bool more = kt + 1 < ntiles;
+    if (more)
+      load_tile<D>(stg, tile_blocks(trow, kt + 1, max_blocks, num_blocks), kc, vc, blk_stride, kvh,
+                   key0 + kBk, n_keys, tid);
+    __syncthreads();  // buffer kt % 2 written; buffer (kt + 1) % 2 no longer read
+    const half_t* cK = sK + (kt & 1) * G::KBUF;
+    const half_t* cVt = sVt + (kt & 1) * G::VBUF;
 
-    if (wq_last < wq_first || key0 > P + wq_last) continue;  // nothing visible to this wave
-
-    // S^T tiles: [st][ks] holds keys key0 + 16 ks + 4 g + i for query row c16
-    float4_t sacc[2][4];
+    if (!(wq_last < wq_first || key0 > P + wq_last)) {  // keys of this tile visible to the wave
+      // S^T tiles: [st][ks] holds keys key0 + 16 ks + 4 g + i for query row c16
+      float4_t sacc[2][4];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sacc[st][ks] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int kk = 0; kk < DK; ++kk) {
-        const half8_t a = *reinterpret_cast<const half8_t*>(&sK[(ks * 16 + c16) * KP + 32 * kk + 8 * g]);
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-          sacc[st][ks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[st][kk], sacc[st][ks], 0, 0, 0);
-      }
-    }
-
-    const bool need_mask = key0 + kBk - 1 > P + wq_first;
-    half_t ph[2][4][4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int lim = P + qrow[st];  // last visible key of this lane's row
-      float mt = -INFINITY;
+        for (int ks = 0; ks < 4; ++ks) sacc[st][ks] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[st][ks][i] * qk_scale;
-          if (need_mask && (key0 + 16 * ks + 4 * g + i) > lim) v = -INFINITY;
-          sacc[st][ks][i] = v;
-          mt = fmaxf(mt, v);
+        for (int kk = 0; kk < G::DK; ++kk) {
+          const half8_t a =
+              *reinterpret_cast<const half8_t*>(&cK[(ks * 16 + c16) * G::KP + 32 * kk + 8 * g]);
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            sacc[st][ks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[st][kk], sacc[st][ks], 0, 0, 0);
         }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m[st], mt);
-      const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2(m[st] - m_new);
-      m[st] = m_new;
-      l[st] *= corr;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[st][dt] *= corr;
-      float ps = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(sacc[st][ks][i] - m_new);
-          ps += pr;
-          ph[st][ks][i] = static_cast<half_t>(pr);
-        }
-      }
-      l[st] += ps;
-    }
 
-    // O^T += V^T P^T over two 32-key pairs of sub-tiles (0,1) and (2,3)
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      half8_t bp[2];
+      const bool need_mask = key0 + kBk - 1 > P + wq_first;
+      half_t ph[2][4][4];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bp[st] = half8_t{ph[st][2 * kp][0], ph[st][2 * kp][1], ph[st][2 * kp][2], ph[st][2 * kp][3],
-                         ph[st][2 * kp + 1][0], ph[st][2 * kp + 1][1], ph[st][2 * kp + 1][2],
-                         ph[st][2 * kp + 1][3]};
+        const int lim = P + qrow[st];  // last visible key of this lane's row
+        float mt = -INFINITY;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = sacc[st][ks][i] * qk_scale;
+            if (need_mask && (key0 + 16 * ks + 4 * g + i) > lim) v = -INFINITY;
+            sacc[st][ks][i] = v;
+            mt = fmaxf(mt, v);
+          }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m[st], mt);
+        // rescale only when some row's max grew (a wave-uniform test)
+        if (__ballot(m_new > m[st]) != 0) {
+          const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2(m[st] - m_new);
+          l[st] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt) o[st][dt] *= corr;
+        }
+        m[st] = m_new;
+        float ps = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = fast_exp2(sacc[st][ks][i] - m_new);
+            ps += pr;
+            ph[st][ks][i] = static_cast<half_t>(pr);
+          }
+        }
+        l[st] += ps;
       }
+
+      // O^T += V^T P^T over two 32-key pairs of sub-tiles (0,1) and (2,3)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const half_t* vrow = &sVt[(dt * 16 + c16) * VP + kp * 32 + 4 * g];
-        const half4_t a0 = *reinterpret_cast<const half4_t*>(vrow);
-        const half4_t a1 = *reinterpret_cast<const half4_t*>(vrow + 16);
-        const half8_t a = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      for (int kp = 0; kp < 2; ++kp) {
+        half8_t bp[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          o[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[st], o[st][dt], 0, 0, 0);
+        for (int st = 0; st < 2; ++st) {
+          bp[st] = half8_t{ph[st][2 * kp][0], ph[st][2 * kp][1], ph[st][2 * kp][2], ph[st][2 * kp][3],
+                           ph[st][2 * kp + 1][0], ph[st][2 * kp + 1][1], ph[st][2 * kp + 1][2],
+                           ph[st][2 * kp + 1][3]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) {
+          const half8_t a =
+              *reinterpret_cast<const half8_t*>(&cVt[(dt * 16 + c16) * G::VP + kp * 32 + 8 * g]);
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            o[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[st], o[st][dt], 0, 0, 0);
+        }
       }
     }
+    if (more) store_tile<D>(stg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF, tid);
   }
 
 #pragma unroll
@@ -213,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const float inv = 1.0f / lt;
     float* orow = out + (static_cast<int64_t>(row0 + qrow[st]) * Hq + h) * D + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < G::DT; ++dt) {
       *reinterpret_cast<float4_t*>(orow + dt * 16) = o[st][dt] * inv;
     }
   }
@@ -228,17 +390,18 @@ hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t to
   if (B <= 0 || max_chunk <= 0 || total_q <= 0) return hipSuccess;
   const int32_t nqt = (max_chunk + kBq - 1) / kBq;
   const float qk_scale = scale * kLog2e;
-  const dim3 grid(nqt, Hq, B);
+  const int64_t pairs = static_cast<int64_t>(B) * Hq;
+  const dim3 grid(static_cast<uint32_t>((pairs + kXcds - 1) / kXcds * kXcds * nqt));
   if (c.head_dim == 128) {
     prefill_kernel<128><<<grid, dim3(kThreads), 0, s>>>(
         static_cast<const half_t*>(q), static_cast<const half_t*>(c.k),
-        static_cast<const half_t*>(c.v), cu_q, prior, tables, out, Hq, c.num_kv_heads, total_q,
-        max_blocks, c.num_blocks, qk_scale);
+        static_cast<const half_t*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
+        max_blocks, c.num_blocks, nqt, qk_scale);
   } else {
     prefill_kernel<64><<<grid, dim3(kThreads), 0, s>>>(
         static_cast<const half_t*>(q), static_cast<const half_t*>(c.k),
-        static_cast<const half_t*>(c.v), cu_q, prior, tables, out, Hq, c.num_kv_heads, total_q,
-        max_blocks, c.num_blocks, qk_scale);
+        static_cast<const half_t*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
+        max_blocks, c.num_blocks, nqt, qk_scale);
   }
   return hipGetLastError();
 }

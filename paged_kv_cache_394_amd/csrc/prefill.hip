@@ -11,24 +11,28 @@
 // Tiling.  A workgroup owns 128 query rows of one (sequence, head): 4 wave64s of
 // 32 rows (two 16-row sub-tiles).  Keys are walked in tiles of 64 (four 16-token
 // blocks looked up in the block table), staged through LDS: K row-major, V
-// transposed, so both MFMA operands are read as short contiguous runs.
+// transposed, so both MFMA operands are read as 16-byte LDS runs.
 // Each wave computes S^T = K Q^T (so a lane ends up holding the scores of one
 // query row, which makes the row max / sum and the output rescale lane-local up
 // to two cross-lane steps) and then O^T = V^T P^T with P taken straight from the
 // S^T registers: the 32-key contraction of one MFMA is permuted so that lane
 // group g's 8 slots are keys {4g..4g+3} and {16+4g..16+4g+3} of a 32-key pair,
-// exactly the scores that lane already holds; the V^T operand is read with the
-// same permutation.  Online softmax in the log2 domain, fp32 statistics, P
-// rounded to fp16 for the MFMA, fp32 accumulation.  The causal mask is applied
-// only on tiles that cross the diagonal.
+// exactly the scores that lane already holds; V^T is stored in LDS in that key
+// order.  Online softmax in the log2 domain with fp32 statistics; the running
+// max is only moved (and the output rescaled) when a row's max grows by more
+// than 2^8, so P <= 2^8 stays well inside fp16; P is rounded to fp16 for the
+// MFMA, fp32 accumulation.  The causal mask is applied only on tiles that
+// cross the diagonal.
 //
 // Staging.  The K/V tiles are double-buffered in LDS: the global loads of tile
 // t+1 are issued into registers before tile t is computed and written to the
 // other buffer after it, so one barrier per tile separates the phases.  The
-// tile's 4 block ids are read with scalar loads, so every address is a scalar
-// block base plus a per-thread constant.  V is transposed in registers on the
-// way: a thread loads 8 keys x 4 columns (8-byte loads) and writes 4 rows of
-// V^T, in a key order that makes each MFMA operand one 16-byte LDS read.
+// tile's 4 block ids are read with scalar loads, and every load of a wave falls
+// in one block, so each address is a scalar block base plus a per-thread
+// constant.  V is transposed in registers: a thread loads 8 keys x 4 columns
+// (8-byte loads) and writes 4 rows of V^T; 16-byte column groups of V^T are
+// XOR-swizzled by row bits 4..6 so that these stores spread over the LDS banks
+// while the MFMA operand reads stay conflict-free.
 //
 // Order.  Workgroups are dispatched longest sequence first (prior + chunk;
 // every workgroup ranks the <= 64 sequences itself), and the query tiles of one
@@ -49,30 +53,35 @@ constexpr int kBq = 128;       // query rows per workgroup
 constexpr int kBk = 64;        // keys per tile
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;       // workgroup ids are dealt round robin over 8 XCDs
+constexpr float kLazyRescale = 8.0f;  // log2 growth of a row max that forces a rescale
 
 template <int D>
 struct PGeom {
   static constexpr int KP = D + 8;          // LDS row stride of K (halfs)
   // LDS row stride of V^T (halfs).  Within each 32-key pair of a V^T row,
-  // key 16 hb + 4 g + i (hb < 2, g < 4, i < 4) is stored at 8 g + 4 hb + i, so
-  // the 8 keys lane group g feeds to one P.V MFMA are one 16-byte run.
+  // key 16 hb + 4 g + i (hb < 2, g < 4, i < 4) sits at 8 g + 4 hb + i, so the
+  // 8 keys lane group g feeds to one P.V MFMA are one 16-byte granule; the 8
+  // granules of row r are stored in order granule ^ ((r / 16) & 7), which is
+  // constant over the 16 rows one read instruction covers (reads stay
+  // conflict-free) and spreads the transposing stores (2-way at most).
   static constexpr int VP = kBk + 8;
   static constexpr int DK = D / 32;         // MFMA steps over head_dim for S
   static constexpr int DT = D / 16;         // 16-wide output tiles over head_dim
   static constexpr int CPR = D / 8;         // 16-byte chunks per K row
-  static constexpr int KLOADS = kBk * CPR / kThreads;        // K chunks per thread
-  static constexpr int VCOMBOS = (kBk / 8) * (D / 4);          // (8 keys x 4 columns) groups
-  static constexpr int VLOADS = (VCOMBOS + kThreads - 1) / kThreads;
+  static constexpr int KLOADS = kBk * CPR / kThreads;  // K chunks per thread
+  static constexpr int VLANES = D / 2;      // lanes of a wave staging V (2 key groups)
   static constexpr int KBUF = kBk * KP;     // halfs per K buffer
   static constexpr int VBUF = D * VP;       // halfs per V^T buffer
   static_assert(kBk * CPR % kThreads == 0, "K tile must split evenly");
+  static_assert(16 * CPR % 64 == 0, "a wave's K chunks must stay in one block");
+  static_assert(VLANES <= 64, "V groups of a block must fit one wave");
 };
 
 // Registers holding one K/V tile between its global loads and its LDS stores.
 template <int D>
 struct Stage {
   u32x4_t k[PGeom<D>::KLOADS];
-  u32x2_t v[PGeom<D>::VLOADS][8];
+  u32x2_t v[8];
 };
 
 // Rank of lane b's sequence (b < B <= 64) by total length, longest first,
@@ -86,15 +95,15 @@ __device__ __forceinline__ int work_rank(int Wb, int lane, int B) {
   return lane < B ? rank : 64;
 }
 
-// The 4 block ids of key tile kt (wave-uniform scalar loads; ids past the
+// The 4 block ids of a key tile (wave-uniform scalar loads; ids past the
 // table's end, or outside the pool, read as block 0), as four scalars.
 struct TileBlocks {
   int p0, p1, p2, p3;
 };
 
-// Block j (0..3, may differ per lane) of a tile.  A free function on values:
-// as a member reading this->pN the selects are folded into one indexed load
-// and the struct is left in memory.
+// Block j (0..3) of a tile.  A free function on values: as a member reading
+// this->pN the selects are folded into one indexed load and the struct is
+// left in memory.
 __device__ __forceinline__ int pick_block(int j, int p0, int p1, int p2, int p3) {
   const int lo = (j & 1) ? p1 : p0;
   const int hi = (j & 1) ? p3 : p2;
@@ -117,81 +126,91 @@ __device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ tr
                     table_id(trow, j0 + 3, max_blocks, num_blocks)};
 }
 
-// Issue the global loads of key tile key0 .. key0 + kBk - 1 (keys at or past
-// n_keys load zeros).  blk_stride: halfs per physical block of one cache.
-// K load i of thread t is 16-byte chunk i * 256 + t of the tile, i.e. key
-// (i * 256 + t) / CPR, in the tile's block i * 256 / (16 CPR) + t / (16 CPR)
-// (the first term is a constant); the thread's V group is 8 consecutive keys
-// of one block and 4 columns.
+// Per-thread staging geometry.  K load i of thread t is 16-byte chunk
+// i * 256 + t of the tile: key (i * 256 + t) / CPR, which lies in block
+// (i * 256 + 64 w) / (16 CPR) of the tile for wave w (the same for the whole
+// wave) at the same in-block row and column for every i.  Wave w stages the V
+// of block w: lane l < D/2 takes key group 2 w + l / (D/4) (8 keys) and
+// columns 4 (l % (D/4)) .. +3.
 template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const TileBlocks& tb,
+struct StageGeom {
+  int k_off;    // halfs from a block's (kv head) base to the thread's K chunk
+  int k_row;    // the chunk's key within the tile, for i = 0 (adds 256 i / CPR)
+  int k_col;    // its first column
+  bool v_on;    // lane stages V
+  int kg, dq;   // key group (0..7) and column quad of the V group
+  int v_off;    // halfs from a block's (kv head) base to key row 0 of the group
+
+  __device__ void init(int tid, int kvh) {
+    using G = PGeom<D>;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    k_row = tid / G::CPR;
+    k_col = (tid % G::CPR) * 8;
+    k_off = (kvh * kBlock + (k_row & 15)) * D + k_col;
+    v_on = lane < G::VLANES;
+    kg = 2 * w + lane / (D / 4);
+    dq = lane % (D / 4);
+    v_off = (kvh * kBlock + 8 * (kg & 1)) * D + 4 * dq;
+  }
+};
+
+// Issue the global loads of a key tile.  Every load stays inside the pool;
+// rows past the context are fixed up by store_tile.
+template <int D>
+__device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D>& sg, const TileBlocks& tb,
                                           const half_t* __restrict__ kc,
                                           const half_t* __restrict__ vc, int64_t blk_stride,
-                                          int kvh, int key0, int n_keys, int tid) {
+                                          int w) {
   using G = PGeom<D>;
 #pragma unroll
   for (int i = 0; i < G::KLOADS; ++i) {
-    const int cidx = i * kThreads + tid;
-    const int key = cidx / G::CPR;
-    const int blk = (i * kThreads) / (kBlock * G::CPR) + tid / (kBlock * G::CPR);
-    const int off = ((kvh * kBlock + (key & 15)) * D) + (cidx % G::CPR) * 8;
-    st.k[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (key0 + key < n_keys)
-      st.k[i] = *reinterpret_cast<const u32x4_t*>(kc + static_cast<int64_t>(pick_block(blk, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride + off);
+    const int blk = (i * kThreads + 64 * w) / (kBlock * G::CPR);  // wave-uniform
+    const half_t* base = kc + static_cast<int64_t>(pick_block(blk, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
+    st.k[i] = *reinterpret_cast<const u32x4_t*>(base + sg.k_off);
   }
+  if (sg.v_on) {
+    const half_t* base = vc + static_cast<int64_t>(pick_block(w, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
 #pragma unroll
-  for (int i = 0; i < G::VLOADS; ++i) {
-    const int combo = i * kThreads + tid;
-    const int kg = combo % (kBk / 8);
-    const int dq = combo / (kBk / 8);
-    const int off = (kvh * kBlock + 8 * (kg & 1)) * D + 4 * dq;
-    const half_t* src = vc + static_cast<int64_t>(pick_block(kg >> 1, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride + off;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      st.v[i][r] = u32x2_t{0u, 0u};
-      if (combo < G::VCOMBOS && key0 + 8 * kg + r < n_keys)
-        st.v[i][r] = *reinterpret_cast<const u32x2_t*>(src + r * D);
-    }
+    for (int r = 0; r < 8; ++r) st.v[r] = *reinterpret_cast<const u32x2_t*>(base + sg.v_off + r * D);
   }
 }
 
-// Write a staged tile to one LDS buffer: K row-major, V transposed.
+// Write a staged tile to one LDS buffer: K row-major, V transposed.  On the
+// tile holding the end of the keys (tail), V rows at or past n_keys are zeroed
+// (their P is 0, but stale cache rows may hold non-finite bits); K rows there
+// only produce scores that the causal mask removes.
 template <int D>
-__device__ __forceinline__ void store_tile(const Stage<D>& st, half_t* __restrict__ sK,
-                                           half_t* __restrict__ sVt, int tid) {
+__device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D>& sg, half_t* __restrict__ sK,
+                                           half_t* __restrict__ sVt, bool tail, int key0, int n_keys) {
   using G = PGeom<D>;
 #pragma unroll
-  for (int i = 0; i < G::KLOADS; ++i) {
-    const int cidx = i * kThreads + tid;
-    const int key = cidx / G::CPR;
-    const int d0 = (cidx % G::CPR) * 8;
-    *reinterpret_cast<u32x4_t*>(&sK[key * G::KP + d0]) = st.k[i];
+  for (int i = 0; i < G::KLOADS; ++i)
+    *reinterpret_cast<u32x4_t*>(&sK[(sg.k_row + i * (kThreads / G::CPR)) * G::KP + sg.k_col]) = st.k[i];
+  if (!sg.v_on) return;
+  if (tail) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (key0 + 8 * sg.kg + r >= n_keys) st.v[r] = u32x2_t{0u, 0u};
   }
+  const int g0 = (sg.kg >> 2) * 4 + 2 * (sg.kg & 1);  // first of the group's two granules
+  const int in_gran = 4 * ((sg.kg >> 1) & 1);
+  const int sw = (sg.dq >> 2) & 7;                     // (row / 16) & 7 for rows 4 dq + j
 #pragma unroll
-  for (int i = 0; i < G::VLOADS; ++i) {
-    const int combo = i * kThreads + tid;
-    if (combo >= G::VCOMBOS) continue;
-    const int kg = combo % (kBk / 8);
-    const int dq = combo / (kBk / 8);
-    // row j of the 4 columns: halves j of the 8 keys, packed two keys a word
+  for (int j = 0; j < 4; ++j) {
+    // column 4 dq + j of the 8 keys, two keys a word: half j & 1 of word j / 2
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t row;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4_t row;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = st.v[i][2 * w][j >> 1];
-        const uint32_t b = st.v[i][2 * w + 1][j >> 1];
-        row[w] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      // keys 8 kg .. 8 kg + 7 of the permuted row (see PGeom): two runs of 4
-      const int base = (4 * dq + j) * G::VP + (kg >> 2) * 32 + 16 * (kg & 1) + 4 * ((kg >> 1) & 1);
-      *reinterpret_cast<u32x2_t*>(&sVt[base]) = u32x2_t{row[0], row[1]};
-      *reinterpret_cast<u32x2_t*>(&sVt[base + 8]) = u32x2_t{row[2], row[3]};
-    }
+    for (int wd = 0; wd < 4; ++wd)
+      row[wd] = __builtin_amdgcn_perm(st.v[2 * wd + 1][j >> 1], st.v[2 * wd][j >> 1], sel);
+    half_t* r0 = &sVt[(4 * sg.dq + j) * G::VP + in_gran];
+    *reinterpret_cast<u32x2_t*>(r0 + ((g0 ^ sw) << 3)) = u32x2_t{row[0], row[1]};
+    *reinterpret_cast<u32x2_t*>(r0 + (((g0 + 1) ^ sw) << 3)) = u32x2_t{row[2], row[3]};
   }
 }
 
-// grid (ceil(B * Hq / 8) * 8 * nqt), block 256.
+// grid (ceil(B * Hq / 8) * 8 * nqt), block 256.  qk_scale = softmax scale * log2 e.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
@@ -205,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
@@ -236,6 +255,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int kvh = h / (Hq / Hkv);
   const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
 
+  // Scores are kept in raw units and scaled inside the exponent by c > 0; a
+  // negative scale flips the sign of q instead (exact).  A zero scale becomes
+  // 1e-30, which leaves every exp2 of a finite score at 1 and keeps masked
+  // scores at -inf (a zero factor would turn them into NaN).
+  const bool neg = qk_scale < 0.f;
+  const float c = fmaxf(neg ? -qk_scale : qk_scale, 1e-30f);
+
   // Q as the B operand of S^T = K Q^T: lane holds q[row = c16][d = 32 kk + 8 g .. +8]
   half8_t qb[2][G::DK];
   int qrow[2];
@@ -247,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const half_t* qp = q + (static_cast<int64_t>(row0 + qrow[st]) * Hq + h) * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < G::DK; ++kk) {
-      qb[st][kk] = qvalid[st] ? *reinterpret_cast<const half8_t*>(qp + 32 * kk) : half8_t{};
+      half8_t v = qvalid[st] ? *reinterpret_cast<const half8_t*>(qp + 32 * kk) : half8_t{};
+      qb[st][kk] = neg ? -v : v;
     }
   }
 
@@ -266,20 +293,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int n_keys = min(P + min(q0 + kBq, C), L_total);  // keys any row of the group needs
   const int ntiles = (n_keys + kBk - 1) / kBk;
 
+  StageGeom<D> sg;
+  sg.init(tid, kvh);
   const int64_t blk_stride = static_cast<int64_t>(Hkv) * kBlock * D;
   Stage<D> stg;
   if (ntiles > 0) {
-    load_tile<D>(stg, tile_blocks(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, kvh, 0,
-                 n_keys, tid);
-    store_tile<D>(stg, sK, sVt, tid);
+    load_tile<D>(stg, sg, tile_blocks(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
+    store_tile<D>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
   }
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int key0 = kt * kBk;
     const bool more = kt + 1 < ntiles;
     if (more)
-      load_tile<D>(stg, tile_blocks(trow, kt + 1, max_blocks, num_blocks), kc, vc, blk_stride, kvh,
-                   key0 + kBk, n_keys, tid);
+      load_tile<D>(stg, sg, tile_blocks(trow, kt + 1, max_blocks, num_blocks), kc, vc, blk_stride, w);
     __syncthreads();  // buffer kt % 2 written; buffer (kt + 1) % 2 no longer read
     const half_t* cK = sK + (kt & 1) * G::KBUF;
     const half_t* cVt = sVt + (kt & 1) * G::VBUF;
@@ -303,39 +330,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         }
       }
 
-      const bool need_mask = key0 + kBk - 1 > P + wq_first;
+      if (key0 + kBk - 1 > P + wq_first) {  // tile crosses the diagonal of some row
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int lim = P + qrow[st];  // last visible key of this lane's row
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key0 + 16 * ks + 4 * g + i > lim) sacc[st][ks][i] = -INFINITY;
+        }
+      }
+
       half_t ph[2][4][4];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int lim = P + qrow[st];  // last visible key of this lane's row
         float mt = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = sacc[st][ks][i] * qk_scale;
-            if (need_mask && (key0 + 16 * ks + 4 * g + i) > lim) v = -INFINITY;
-            sacc[st][ks][i] = v;
-            mt = fmaxf(mt, v);
-          }
-        }
+        for (int ks = 0; ks < 4; ++ks)
+          mt = fmaxf(mt, fmaxf(fmaxf(sacc[st][ks][0], sacc[st][ks][1]),
+                               fmaxf(sacc[st][ks][2], sacc[st][ks][3])));
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m[st], mt);
-        // rescale only when some row's max grew (a wave-uniform test)
-        if (__ballot(m_new > m[st]) != 0) {
-          const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2(m[st] - m_new);
+        // move the running max (and rescale) only when some row's max grew by
+        // more than 2^kLazyRescale: exp2 arguments stay <= kLazyRescale
+        const float grow = (mt - m[st]) * c;  // +inf on the first visible tile
+        if (__ballot(grow > kLazyRescale) != 0) {
+          const float m_new = fmaxf(m[st], mt);
+          const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2((m[st] - m_new) * c);
           l[st] *= corr;
 #pragma unroll
           for (int dt = 0; dt < G::DT; ++dt) o[st][dt] *= corr;
+          m[st] = m_new;
         }
-        m[st] = m_new;
+        const float mc = (m[st] == -INFINITY) ? 0.f : m[st] * c;
         float ps = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pr = fast_exp2(sacc[st][ks][i] - m_new);
+            const float pr = fast_exp2(fmaf(sacc[st][ks][i], c, -mc));
             ps += pr;
             ph[st][ks][i] = static_cast<half_t>(pr);
           }
@@ -355,15 +389,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         }
 #pragma unroll
         for (int dt = 0; dt < G::DT; ++dt) {
+          const int gran = (kp * 4 + g) ^ (dt & 7);  // rows 16 dt + c16: swizzle dt & 7
           const half8_t a =
-              *reinterpret_cast<const half8_t*>(&cVt[(dt * 16 + c16) * G::VP + kp * 32 + 8 * g]);
+              *reinterpret_cast<const half8_t*>(&cVt[(dt * 16 + c16) * G::VP + (gran << 3)]);
 #pragma unroll
           for (int st = 0; st < 2; ++st)
             o[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[st], o[st][dt], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile<D>(stg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF, tid);
+    if (more)
+      store_tile<D>(stg, sg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF,
+                    key0 + 2 * kBk > n_keys, key0 + kBk, n_keys);
   }
 
 #pragma unroll

@@ -75,9 +75,9 @@ class DecodeCase:
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.out = torch.empty((len(self.ids), w.num_heads, w.head_dim), dtype=torch.float32, device=device)
 
-    def decode(self):
-        pa.pa_decode(self.cache, self.q, self.tables, self.lens, self.max_ctx, self.w.scale,
-                     self.out, self.ws)
+    def decode(self, scale=None):
+        pa.pa_decode(self.cache, self.q, self.tables, self.lens, self.max_ctx,
+                     self.w.scale if scale is None else scale, self.out, self.ws)
         torch.cuda.synchronize()
         return self.out.cpu().numpy()
 
@@ -95,7 +95,7 @@ def fp8_scales(w, seqs):
     return float(ks), float(vs)
 
 
-def oracle_decode(w, pairs, seqs=None, fp8_scales_=None):
+def oracle_decode(w, pairs, seqs=None, fp8_scales_=None, scale=None):
     """float64 reference for (i, h) pairs, i indexing ``seqs``.  With fp8 scales
     the reference attends over the quantised-then-dequantised K/V."""
     seqs = list(range(w.batch)) if seqs is None else list(seqs)
@@ -112,5 +112,5 @@ def oracle_decode(w, pairs, seqs=None, fp8_scales_=None):
             cache[b] = (np.asarray(k, dtype=np.float64), np.asarray(v, dtype=np.float64))
         k, v = cache[b]
         kh = h // (w.num_heads // w.num_kv_heads)
-        out[(i, h)] = attention_fp64(w.q[b, h], k[:, kh], v[:, kh], w.scale)
+        out[(i, h)] = attention_fp64(w.q[b, h], k[:, kh], v[:, kh], w.scale if scale is None else scale)
     return out

@@ -151,3 +151,60 @@ def test_llama13b_fp8_sampled():
     for (i, h), r in ref16.items():
         close(got[i, h], r, ATOL8, ATOL8)
     assert np.isfinite(got).all()
+
+
+def test_wide_batch_beyond_64_sequences_per_sequence_path():
+    """128 sequences x 16 heads: enough (sequence, head) pairs for one workgroup
+    per pair, and too many sequences for the in-wave longest-first ranking, so
+    the pairs keep their index order."""
+    rng = np.random.default_rng(141)
+    lens = rng.integers(1, 600, size=128)
+    w = workloads.custom_decode(141, lens, 16, 16, 128)
+    check_full(DecodeCase(w))
+
+
+def test_split_path_beyond_64_sequences_grouped_heads():
+    """80 sequences, 4 query heads over 2 KV heads, contexts up to 3000 tokens:
+    the split-K path with its merge kernel, units in index order (B > 64)."""
+    rng = np.random.default_rng(151)
+    lens = rng.integers(1, 3000, size=80)
+    lens[::9] = 0
+    w = workloads.custom_decode(151, lens, 4, 2, 128)
+    case = DecodeCase(w)
+    got = case.decode()
+    assert np.all(got[::9] == 0)
+    check_full(case)
+
+
+def test_eight_wave_path_with_empty_contexts_and_tied_lengths():
+    """30 sequences x 40 heads takes the per-sequence path with 8 waves per
+    workgroup; equal lengths exercise the ranking's tie break and empty
+    contexts must come out as zeros."""
+    lens = [700, 700, 0, 33, 700, 1, 0, 250, 251, 250] * 3
+    w = workloads.custom_decode(161, lens, 40, 40, 64)
+    case = DecodeCase(w)
+    got = case.decode()
+    for i, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[i] == 0)
+    check_full(case)
+
+
+@pytest.mark.parametrize("scale", [-0.05, 0.0])
+def test_decode_nonpositive_scale(scale):
+    """Split and per-sequence paths with a negative and a zero softmax scale."""
+    for lens, heads in (([3, 40, 517], 4), ([90] * 64, 32)):
+        w = workloads.custom_decode(171, lens, heads, heads, 128)
+        case = DecodeCase(w)
+        got = case.decode(scale)
+        pairs = [(i, h) for i in range(len(lens)) for h in range(heads)]
+        ref = oracle_decode(w, pairs, scale=scale)
+        R = np.stack([np.stack([ref[(i, h)] for h in range(heads)]) for i in range(len(lens))])
+        close(got, R)
+
+
+def test_long_context_many_splits():
+    """Contexts of up to 9000 tokens in a narrow batch: 18 splits of 512 tokens,
+    more than the merge kernel loads up front (8), so its looped pass runs."""
+    w = workloads.custom_decode(181, [9000, 5000, 8193], 2, 2, 128)
+    check_full(DecodeCase(w))

@@ -43,29 +43,29 @@ class PrefillCase:
         self.out = torch.full((int(cu[-1]), w.num_heads, w.head_dim), float("nan"),
                               dtype=torch.float32, device="cuda")
 
-    def run(self):
+    def run(self, scale=None):
         pa.pa_prefill_chunk(self.cache, self.q, self.cu, self.prior, self.tables,
-                            int(self.w.chunk.max()), self.w.scale, self.out)
+                            int(self.w.chunk.max()), self.w.scale if scale is None else scale, self.out)
         torch.cuda.synchronize()
         return self.out.cpu().numpy()
 
-    def ref_row(self, b, i, h):
+    def ref_row(self, b, i, h, scale=None):
         w = self.w
         k, v = w.kv(b, cache=True)
         kh = h // (w.num_heads // w.num_kv_heads)
         n = int(w.prior[b]) + i + 1
         r = int(self.cu_np[b]) + i
-        return attention_fp64(w.q[r, h], k[:n, kh], v[:n, kh], w.scale)
+        return attention_fp64(w.q[r, h], k[:n, kh], v[:n, kh], w.scale if scale is None else scale)
 
 
-def check_all(case):
-    got = case.run()
+def check_all(case, scale=None):
+    got = case.run(scale)
     w = case.w
     for b in range(w.batch):
         for i in range(int(w.chunk[b])):
             r = int(case.cu_np[b]) + i
             for h in range(w.num_heads):
-                close(got[r, h], case.ref_row(b, i, h))
+                close(got[r, h], case.ref_row(b, i, h, scale))
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -102,3 +102,11 @@ def test_chunked_prefill_full_size_sampled():
         for i in rows:
             for h in (0, 21, 39):
                 close(got[int(case.cu_np[b]) + i, h], case.ref_row(b, i, h))
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.5])
+def test_prefill_any_finite_scale(scale):
+    """The kernel keeps scores in raw units and scales inside the exponent; a
+    negative scale flips q, a zero scale gives the mean of the visible values."""
+    w = workloads.custom_prefill(131, [20, 0], [40, 70], 2, 2, 128)
+    check_all(PrefillCase(w), scale)

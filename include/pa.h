@@ -144,6 +144,14 @@ pa_status pa_block_tables(const pa_pool *pool, const int32_t *seqs, int32_t n,
 pa_status pa_seq_table(const pa_pool *pool, int32_t seq, int32_t *table_out, int32_t cap,
                        int32_t *n_out, int32_t *len_out);
 
+/* For each of n sequences, the number of leading table entries whose block is
+ * shared (ref_cnt > 1), into host int32[n].  Forked sequences share a prefix of
+ * their tables ([p3] copy-on-write section: one stored copy of a common prompt),
+ * so these counts mark the blocks every sharer reads; pa_decode can read those
+ * through the caches (cached_blocks_dev).  Errors: BAD_SEQ, BAD_ARG. */
+pa_status pa_shared_prefix(const pa_pool *pool, const int32_t *seqs, int32_t n,
+                           int32_t *blocks_out);
+
 /* Snapshot of the pool: counters, and optionally the free queue from front to back
  * (host int32[num_blocks], first free_blocks entries valid) and ref_cnt
  * (host int32[num_blocks]).  Either array may be NULL. */
@@ -179,16 +187,22 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
  * out[b][h] = softmax(scale * K_b q[b][h]) V_b over tokens 0..lens[b]-1 of KV head
  * h / (num_heads / num_kv_heads).  Sequences with lens[b] == 0 get zeros.
  * q: device fp16 [B][num_heads][head_dim].  tables_dev: device int32[B][max_blocks]
- * (as from pa_block_tables).  lens_dev: device int32[B].  max_context_len: an upper
- * bound on every lens[b] (sizes the split-K grid).  out_dev: device fp32
- * [B][num_heads][head_dim].  workspace: at least pa_decode_workspace_bytes(...).
+ * (as from pa_block_tables).  lens_dev: device int32[B].  cached_blocks_dev: NULL,
+ * or device int32[B] (as from pa_shared_prefix): a read-pattern hint only, the
+ * result does not depend on it.  K/V are streamed with non-temporal loads, since
+ * each byte is read once per call, except the first cached_blocks[b] blocks of
+ * sequence b, which other sequences of the batch also read and which are read
+ * through the caches.  max_context_len: an upper bound on every lens[b] (sizes
+ * the launch).  out_dev: device fp32 [B][num_heads][head_dim].  workspace: at
+ * least pa_decode_workspace_bytes(...) (used only by batches too narrow to fill
+ * the GPU with one workgroup per (sequence, head)).
  * Errors: BAD_ARG (shape, null pointers, num_heads % num_kv_heads, workspace too
  * small), UNSUPPORTED (block_size != 16, head_dim not 64/128), HIP. */
 pa_status pa_decode(const pa_kv_cache *cache, const void *q, int32_t num_heads,
-                    const int32_t *tables_dev, const int32_t *lens_dev, int32_t B,
-                    int32_t max_blocks, int32_t max_context_len, float scale,
-                    float *out_dev, void *workspace_dev, size_t workspace_bytes,
-                    void *hip_stream);
+                    const int32_t *tables_dev, const int32_t *lens_dev,
+                    const int32_t *cached_blocks_dev, int32_t B, int32_t max_blocks,
+                    int32_t max_context_len, float scale, float *out_dev, void *workspace_dev,
+                    size_t workspace_bytes, void *hip_stream);
 
 /* Chunked-prefill attention over the paged cache ([p1] "Chunked Prefill" and
  * "Mechanics of Chunked Prefill"): the chunk's K/V must already be written (by

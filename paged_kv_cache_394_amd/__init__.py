@@ -75,12 +75,14 @@ _SIGNATURES = {
     "pa_seq_free": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "pa_block_tables": (ctypes.c_int32, [ctypes.c_void_p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
     "pa_seq_table": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
+    "pa_shared_prefix": (ctypes.c_int32, [ctypes.c_void_p, _i32p, ctypes.c_int32, _i32p]),
     "pa_pool_state": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(pa_pool_stats), _i32p, _i32p]),
     "pa_write_kv": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_void_p]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 4),
     "pa_decode": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_int32,
-                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]),
     "pa_prefill_chunk": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_int32,
@@ -193,6 +195,14 @@ def pa_seq_table(pool: Pool, seq: int) -> Tuple[np.ndarray, int]:
     return t, ln.value
 
 
+def pa_shared_prefix(pool: Pool, seqs: Sequence[int]) -> np.ndarray:
+    """Leading shared (ref_cnt > 1) table entries of each sequence, int32[n]."""
+    s = _i32(seqs)
+    out = np.empty(len(s), dtype=np.int32)
+    _check(lib.pa_shared_prefix(pool.handle, _p(s), len(s), _p(out)))
+    return out
+
+
 def pa_pool_state(pool: Pool):
     """Returns (stats dict, free queue front-to-back list, ref_cnt int32[N])."""
     st = pa_pool_stats()
@@ -264,13 +274,16 @@ def pa_decode_workspace_bytes(B: int, num_heads: int, head_dim: int, max_context
 
 def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch.Tensor,
               max_context_len: int, scale: float, out: torch.Tensor,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+              workspace: Optional[torch.Tensor] = None, stream=None,
+              cached_blocks: Optional[torch.Tensor] = None) -> None:
     """q [B][Hq][D] float16, tables int32[B][max_blocks], lens int32[B] (device),
-    out float32 [B][Hq][D], workspace a device byte tensor."""
+    out float32 [B][Hq][D], workspace a device byte tensor, cached_blocks None or
+    device int32[B] (from pa_shared_prefix; a read hint, not an input)."""
     B, Hq, D = q.shape
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    cb = None if cached_blocks is None else _dev(cached_blocks, torch.int32)
     _check(lib.pa_decode(ctypes.byref(cache.desc), _dev(q, torch.float16), Hq,
-                         _dev(tables, torch.int32), _dev(lens, torch.int32), B, tables.shape[1],
+                         _dev(tables, torch.int32), _dev(lens, torch.int32), cb, B, tables.shape[1],
                          max_context_len, scale, _dev(out, torch.float32), ws_ptr, ws_bytes,
                          _stream(stream)))
 

@@ -86,9 +86,10 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
 }
 
 pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
-                    const int32_t* tables_dev, const int32_t* lens_dev, int32_t B,
-                    int32_t max_blocks, int32_t max_context_len, float scale, float* out_dev,
-                    void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+                    const int32_t* tables_dev, const int32_t* lens_dev,
+                    const int32_t* cached_blocks_dev, int32_t B, int32_t max_blocks,
+                    int32_t max_context_len, float scale, float* out_dev, void* workspace_dev,
+                    size_t workspace_bytes, void* hip_stream) {
   const char* fn = "pa_decode";
   pa::KvDesc d;
   if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
@@ -109,8 +110,8 @@ pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
     return fail(PA_ERR_BAD_ARG, "pa_decode: workspace smaller than pa_decode_workspace_bytes()");
   if (need > 0 && !aligned16(workspace_dev))
     return fail(PA_ERR_BAD_ARG, "pa_decode: workspace must be 16-byte aligned");
-  return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, B, max_blocks,
-                                      max_context_len, scale, out_dev, workspace_dev,
+  return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, cached_blocks_dev, B,
+                                      max_blocks, max_context_len, scale, out_dev, workspace_dev,
                                       static_cast<hipStream_t>(hip_stream)),
                     fn);
 }

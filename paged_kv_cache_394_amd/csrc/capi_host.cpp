@@ -104,6 +104,15 @@ pa_status pa_seq_table(const pa_pool* pool, int32_t seq, int32_t* table_out, int
   return pa::ok();
 }
 
+pa_status pa_shared_prefix(const pa_pool* pool, const int32_t* seqs, int32_t n,
+                           int32_t* blocks_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_shared_prefix: pool is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->shared_prefix(seqs, n, blocks_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
 pa_status pa_pool_state(const pa_pool* pool, pa_pool_stats* stats_out, int32_t* free_order_out,
                         int32_t* ref_cnt_out) {
   if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_pool_state: pool is NULL");

@@ -29,9 +29,11 @@ int32_t decode_partition_tokens();
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len);
 // Work units (one wave each) of one decode launch; must stay below 2^31.
 int64_t decode_units(int32_t B, int32_t Hq, int32_t max_context_len);
+// cached: NULL or int32[B], leading blocks per sequence read through the caches.
 hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
-                         const int32_t* lens, int32_t B, int32_t max_blocks, int32_t max_context_len,
-                         float scale, float* out, void* workspace, hipStream_t s);
+                         const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
+                         int32_t max_context_len, float scale, float* out, void* workspace,
+                         hipStream_t s);
 
 // Chunked prefill (MFMA).
 hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,

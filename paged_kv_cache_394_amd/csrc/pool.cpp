@@ -239,6 +239,27 @@ Status BlockPool::seq_table(int32_t seq, int32_t* table, int32_t cap, int32_t* n
   return kOk;
 }
 
+Status BlockPool::shared_prefix(const int32_t* seqs, int32_t n, int32_t* out,
+                                std::string* err) const {
+  if (n < 0 || (n > 0 && (seqs == nullptr || out == nullptr))) {
+    *err = "pa_shared_prefix: bad arguments";
+    return kBadArg;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (!live(seqs[i])) {
+      *err = "pa_shared_prefix: unknown sequence";
+      return kBadSeq;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = seqs_[seqs[i]];
+    int32_t k = 0;
+    while (k < static_cast<int32_t>(s.table.size()) && ref_[s.table[k]] > 1) ++k;
+    out[i] = k;
+  }
+  return kOk;
+}
+
 void BlockPool::state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) const {
   if (st) {
     st->num_blocks = n_;

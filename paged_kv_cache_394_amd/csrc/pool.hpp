@@ -47,6 +47,8 @@ class BlockPool {
                       int32_t* lens, std::string* err) const;
   Status seq_table(int32_t seq, int32_t* table, int32_t cap, int32_t* n_out,
                    int32_t* len_out) const;
+  // Per sequence: how many leading table entries are shared (ref_cnt > 1).
+  Status shared_prefix(const int32_t* seqs, int32_t n, int32_t* out, std::string* err) const;
   void state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) const;
 
   int32_t num_blocks() const { return n_; }

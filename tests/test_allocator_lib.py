@@ -21,6 +21,16 @@ def assert_same_state(lib_pool, orc: OraclePool):
     for sid in orc.tables:
         t, ln = pa.pa_seq_table(lib_pool, sid)
         assert t.tolist() == orc.table(sid) and ln == orc.lens[sid]
+    # shared prefix: leading table entries whose block more than one table holds
+    sids = sorted(orc.tables)
+    got = pa.pa_shared_prefix(lib_pool, sids).tolist()
+    want = []
+    for sid in sids:
+        k = 0
+        while k < len(orc.tables[sid]) and orc.ref_cnt[orc.tables[sid][k]] > 1:
+            k += 1
+        want.append(k)
+    assert got == want
 
 
 class Pair:
@@ -124,6 +134,8 @@ def test_shared_prompt_fork_and_cow(prompt, expect_cow):
         cows += cow is not None
     p.check()
     assert cows == expect_cow
+    # every sequence still shares the prompt's full blocks (50 of 16 tokens)
+    assert pa.pa_shared_prefix(p.lib, seqs).tolist() == [50] * 32
     # decode step: one more token each
     for s in seqs:
         p.append(s, 1)
@@ -147,6 +159,10 @@ def test_errors_leave_state_unchanged():
     p.append(77, 1)          # BAD_SEQ
     p.free(77)
     p.fork(77)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_shared_prefix(p.lib, [a, 77])
+    assert e.value.name == "bad_seq"
+    assert pa.pa_shared_prefix(p.lib, []).tolist() == []
     c = p.fork(a)
     p.append(c, 1)           # CoW takes the last block
     d = p.fork(c)

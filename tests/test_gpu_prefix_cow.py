@@ -34,9 +34,10 @@ def build(w, small_heads=None):
     return pool, cache, seqs, n_cow
 
 
-@pytest.mark.parametrize("prompt", [800, 808])
-def test_shared_prompt_decode(prompt):
-    w = workloads.prefix_cow(prompt_len=prompt)
+# 40 heads: one workgroup per (sequence, head); 8 heads: the split path
+@pytest.mark.parametrize("prompt,heads", [(800, 40), (808, 40), (808, 8)])
+def test_shared_prompt_decode(prompt, heads):
+    w = workloads.prefix_cow(prompt_len=prompt, num_heads=heads)
     pool, cache, seqs, n_cow = build(w)
     assert n_cow == (0 if prompt % 16 == 0 else w.batch - 1)
     max_ctx = int(w.lens.max())
@@ -55,9 +56,16 @@ def test_shared_prompt_decode(prompt):
     out = torch.empty((w.batch, w.num_heads, w.head_dim), dtype=torch.float32, device="cuda")
     ws = torch.empty(pa.pa_decode_workspace_bytes(w.batch, w.num_heads, w.head_dim, max_ctx),
                      dtype=torch.uint8, device="cuda")
-    pa.pa_decode(cache, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), max_ctx,
-                 w.scale, out, ws)
+    tables_d, lens_d = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    pa.pa_decode(cache, q, tables_d, lens_d, max_ctx, w.scale, out, ws)
+    # the shared-prefix hint changes only how K/V are read: identical bits
+    shared = pa.pa_shared_prefix(pool, seqs)
+    assert (shared == full).all()
+    out_hint = torch.empty_like(out)
+    pa.pa_decode(cache, q, tables_d, lens_d, max_ctx, w.scale, out_hint, ws,
+                 cached_blocks=torch.from_numpy(shared).cuda())
     torch.cuda.synchronize()
+    assert torch.equal(out, out_hint)
     got = out.cpu().numpy()
     pk, pv = w.prompt_kv()
     rng = np.random.default_rng(prompt)

@@ -19,6 +19,10 @@ Reported on one JSON line:
   host         block-manager call rates
   cpu_baseline the float64 oracle on a bounded sample of the batch (host cores)
 
+Every leg first runs its own work untimed for SETTLE_S seconds, so that the
+GPU is at its steady clock when the W warm-up steps and the timed region
+start (after the host-side set-up of a leg the clock has dropped).
+
 Counter runs: ``--pmc-run`` does only a 256 MiB device copy (torch.neg, one
 elementwise kernel that reads and writes 256 MiB) and a few decode steps, for
 ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE``; ``--summarize-pmc FETCH_DIR
@@ -133,6 +137,21 @@ def setup_decode(w, fp8: bool, pa, torch, np):
     return d
 
 
+SETTLE_S = 0.25  # seconds of untimed work that bring the GPU to its steady clock
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn back to back until `seconds` have passed.  After a pause (the
+    host-side set-up of a leg), the GPU needs tens of milliseconds of load to
+    return to its steady clock; without this a short timed region measures
+    the ramp (the prefill leg reads about 25% slow)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def decode_call(pa, w, d):
     pa.pa_decode(d["cache"], d["q"], d["tables"], d["lens"], d["max_ctx"], w.scale, d["out"], d["ws"],
                  cached_blocks=d.get("cached"))
@@ -148,6 +167,7 @@ def run_decode(pa, torch, w, d, steps, warmup):
         if ev is not None:
             ev[1].record()
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -174,6 +194,7 @@ def decode_bytes(w, elem_bytes, lens=None):
 
 
 def time_events(torch, fn, reps, warmup=3):
+    settle(torch, fn)
     for _ in range(warmup):
         fn()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]

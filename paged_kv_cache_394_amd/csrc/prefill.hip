@@ -19,20 +19,24 @@
 // group g's 8 slots are keys {4g..4g+3} and {16+4g..16+4g+3} of a 32-key pair,
 // exactly the scores that lane already holds; V^T is stored in LDS in that key
 // order.  Online softmax in the log2 domain with fp32 statistics; the running
-// max is only moved (and the output rescaled) when a row's max grows by more
-// than 2^8, so P <= 2^8 stays well inside fp16; P is rounded to fp16 for the
-// MFMA, fp32 accumulation.  The causal mask is applied only on tiles that
-// cross the diagonal.
+// max is only moved (and the output rescaled) when some lane's scores exceed it
+// by more than 2^8, so P <= 2^8 stays well inside fp16.  Each lane tests its
+// own 16 scores; the cross-lane row max is formed only on the (rare) rescale.
+// P is rounded to fp16 for the MFMA, fp32 accumulation.  The causal mask is
+// applied only on tiles that cross the diagonal.
 //
 // Staging.  The K/V tiles are double-buffered in LDS: the global loads of tile
 // t+1 are issued into registers before tile t is computed and written to the
 // other buffer after it, so one barrier per tile separates the phases.  The
-// tile's 4 block ids are read with scalar loads, and every load of a wave falls
-// in one block, so each address is a scalar block base plus a per-thread
-// constant.  V is transposed in registers: a thread loads 8 keys x 4 columns
-// (8-byte loads) and writes 4 rows of V^T; 16-byte column groups of V^T are
-// XOR-swizzled by row bits 4..6 so that these stores spread over the LDS banks
-// while the MFMA operand reads stay conflict-free.
+// block ids of tile t+1 come from a vector load issued one tile earlier, so no
+// scalar-cache wait sits at the top of the loop; every load of a wave falls in
+// one block, so each address is a block base plus a per-thread constant.  V is
+// transposed in registers: a thread loads the 8 keys of one V^T granule x 4
+// columns (8-byte loads) and writes 4 granules of 16 bytes.  Neither buffer is
+// padded: 16-byte chunks are XOR-swizzled by row (K: chunk ^ (row & 15) for
+// head_dim 128; V^T: granule ^ ((row ^ row >> 2) & 7)), layouts that measure
+// free of LDS bank conflicts for both the staging stores and the MFMA operand
+// reads on gfx950.
 //
 // Order.  Workgroups are dispatched longest sequence first (prior + chunk;
 // every workgroup ranks the <= 64 sequences itself), and the query tiles of one
@@ -57,31 +61,38 @@ constexpr float kLazyRescale = 8.0f;  // log2 growth of a row max that forces a 
 
 template <int D>
 struct PGeom {
-  static constexpr int KP = D + 8;          // LDS row stride of K (halfs)
-  // LDS row stride of V^T (halfs).  Within each 32-key pair of a V^T row,
-  // key 16 hb + 4 g + i (hb < 2, g < 4, i < 4) sits at 8 g + 4 hb + i, so the
-  // 8 keys lane group g feeds to one P.V MFMA are one 16-byte granule; the 8
-  // granules of row r are stored in order granule ^ ((r / 16) & 7), which is
-  // constant over the 16 rows one read instruction covers (reads stay
-  // conflict-free) and spreads the transposing stores (2-way at most).
-  static constexpr int VP = kBk + 8;
+  // K is stored row-major without padding; the 16-byte chunk c of key row r
+  // sits at chunk c ^ kswz(r).  V^T rows (one per head-dim column) hold the
+  // tile's 64 keys as 8 granules of 8 keys: granule 4 p + g of a row holds
+  // keys 32 p + 16 hb + 4 g + i (hb < 2, i < 4) at slot 4 hb + i, which is
+  // exactly the 8 keys lane group g feeds to one P.V MFMA; granule q of row r
+  // sits at q ^ vswz(r).  Both swizzles keep the MFMA operand reads and the
+  // staging stores free of bank conflicts.
   static constexpr int DK = D / 32;         // MFMA steps over head_dim for S
   static constexpr int DT = D / 16;         // 16-wide output tiles over head_dim
   static constexpr int CPR = D / 8;         // 16-byte chunks per K row
   static constexpr int KLOADS = kBk * CPR / kThreads;  // K chunks per thread
-  static constexpr int VLANES = D / 2;      // lanes of a wave staging V (2 key groups)
-  static constexpr int KBUF = kBk * KP;     // halfs per K buffer
-  static constexpr int VBUF = D * VP;       // halfs per V^T buffer
+  static constexpr int VTHREADS = 8 * (D / 4);         // threads staging V: granule x column quad
+  static constexpr int KBUF = kBk * D;      // halfs per K buffer
+  static constexpr int VBUF = D * kBk;      // halfs per V^T buffer
   static_assert(kBk * CPR % kThreads == 0, "K tile must split evenly");
   static_assert(16 * CPR % 64 == 0, "a wave's K chunks must stay in one block");
-  static_assert(VLANES <= 64, "V groups of a block must fit one wave");
+  static_assert(VTHREADS <= kThreads && VTHREADS % 64 == 0, "V staging must fill whole waves");
 };
+
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 2)) & 7; }
+
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return swz8(r);
+}
 
 // Registers holding one K/V tile between its global loads and its LDS stores.
 template <int D>
 struct Stage {
   u32x4_t k[PGeom<D>::KLOADS];
-  u32x2_t v[8];
+  u32x2_t v[8];   // keys 4 g + i of block 2 p (v[i]) and of block 2 p + 1 (v[4 + i])
 };
 
 // Rank of lane b's sequence (b < B <= 64) by total length, longest first,
@@ -117,6 +128,25 @@ __device__ __forceinline__ int table_id(const int32_t* __restrict__ trow, int id
   return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
 }
 
+// Lanes 0..3 load the 4 table entries of tile kt (a vector load, waited on
+// in order with the tile loads, one tile ahead of use).
+__device__ __forceinline__ int tile_ids_lanes(const int32_t* __restrict__ trow, int kt, int max_blocks,
+                                              int lane) {
+  const int j = kt * (kBk / kBlock) + lane;
+  return (lane < 4 && j < max_blocks) ? trow[j] : 0;
+}
+
+__device__ __forceinline__ int clamp_id(int v, int num_blocks) {
+  return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
+}
+
+__device__ __forceinline__ TileBlocks tile_blocks_from(int ids, int num_blocks) {
+  return TileBlocks{clamp_id(__builtin_amdgcn_readlane(ids, 0), num_blocks),
+                    clamp_id(__builtin_amdgcn_readlane(ids, 1), num_blocks),
+                    clamp_id(__builtin_amdgcn_readlane(ids, 2), num_blocks),
+                    clamp_id(__builtin_amdgcn_readlane(ids, 3), num_blocks)};
+}
+
 __device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ trow, int kt,
                                                   int max_blocks, int num_blocks) {
   const int j0 = kt * (kBk / kBlock);
@@ -129,29 +159,28 @@ __device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ tr
 // Per-thread staging geometry.  K load i of thread t is 16-byte chunk
 // i * 256 + t of the tile: key (i * 256 + t) / CPR, which lies in block
 // (i * 256 + 64 w) / (16 CPR) of the tile for wave w (the same for the whole
-// wave) at the same in-block row and column for every i.  Wave w stages the V
-// of block w: lane l < D/2 takes key group 2 w + l / (D/4) (8 keys) and
-// columns 4 (l % (D/4)) .. +3.
+// wave) at the same in-block row and column for every i.  Thread t < VTHREADS
+// stages V granule q = t / (D/4) (pair p = q / 4, group g = q % 4) for
+// columns 4 dq .. 4 dq + 3, dq = t % (D/4): rows 4 g .. 4 g + 3 of blocks
+// 2 p and 2 p + 1 of the tile (one pair of blocks per wave).
 template <int D>
 struct StageGeom {
   int k_off;    // halfs from a block's (kv head) base to the thread's K chunk
   int k_row;    // the chunk's key within the tile, for i = 0 (adds 256 i / CPR)
-  int k_col;    // its first column
-  bool v_on;    // lane stages V
-  int kg, dq;   // key group (0..7) and column quad of the V group
-  int v_off;    // halfs from a block's (kv head) base to key row 0 of the group
+  int k_col;    // its chunk index
+  bool v_on;    // thread stages V
+  int vq, dq;   // granule (0..7) and column quad
+  int v_off;    // halfs from a block's (kv head) base to row 4 g, column 4 dq
 
   __device__ void init(int tid, int kvh) {
     using G = PGeom<D>;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
     k_row = tid / G::CPR;
-    k_col = (tid % G::CPR) * 8;
-    k_off = (kvh * kBlock + (k_row & 15)) * D + k_col;
-    v_on = lane < G::VLANES;
-    kg = 2 * w + lane / (D / 4);
-    dq = lane % (D / 4);
-    v_off = (kvh * kBlock + 8 * (kg & 1)) * D + 4 * dq;
+    k_col = tid % G::CPR;
+    k_off = (kvh * kBlock + (k_row & 15)) * D + k_col * 8;
+    v_on = tid < G::VTHREADS;
+    vq = (tid / (D / 4)) & 7;
+    dq = tid % (D / 4);
+    v_off = (kvh * kBlock + 4 * (vq & 3)) * D + 4 * dq;
   }
 };
 
@@ -170,9 +199,14 @@ __device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D>& sg, 
     st.k[i] = *reinterpret_cast<const u32x4_t*>(base + sg.k_off);
   }
   if (sg.v_on) {
-    const half_t* base = vc + static_cast<int64_t>(pick_block(w, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
+    // pair p = vq / 4 is wave-uniform: 64 threads cover 64 / (D/4) granules of one pair
+    const int p = __builtin_amdgcn_readfirstlane(sg.vq >> 2);
+    const half_t* b0 = vc + static_cast<int64_t>(pick_block(2 * p, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
+    const half_t* b1 = vc + static_cast<int64_t>(pick_block(2 * p + 1, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) st.v[r] = *reinterpret_cast<const u32x2_t*>(base + sg.v_off + r * D);
+    for (int i = 0; i < 4; ++i) st.v[i] = *reinterpret_cast<const u32x2_t*>(b0 + sg.v_off + i * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.v[4 + i] = *reinterpret_cast<const u32x2_t*>(b1 + sg.v_off + i * D);
   }
 }
 
@@ -185,28 +219,27 @@ __device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D>& sg,
                                            half_t* __restrict__ sVt, bool tail, int key0, int n_keys) {
   using G = PGeom<D>;
 #pragma unroll
-  for (int i = 0; i < G::KLOADS; ++i)
-    *reinterpret_cast<u32x4_t*>(&sK[(sg.k_row + i * (kThreads / G::CPR)) * G::KP + sg.k_col]) = st.k[i];
+  for (int i = 0; i < G::KLOADS; ++i) {
+    const int r = sg.k_row + i * (kThreads / G::CPR);
+    *reinterpret_cast<u32x4_t*>(&sK[r * D + ((sg.k_col ^ kswz<D>(r)) << 3)]) = st.k[i];
+  }
   if (!sg.v_on) return;
   if (tail) {
+    const int kb = key0 + 32 * (sg.vq >> 2) + 4 * (sg.vq & 3);
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (key0 + 8 * sg.kg + r >= n_keys) st.v[r] = u32x2_t{0u, 0u};
+    for (int s8 = 0; s8 < 8; ++s8)
+      if (kb + 16 * (s8 >> 2) + (s8 & 3) >= n_keys) st.v[s8] = u32x2_t{0u, 0u};
   }
-  const int g0 = (sg.kg >> 2) * 4 + 2 * (sg.kg & 1);  // first of the group's two granules
-  const int in_gran = 4 * ((sg.kg >> 1) & 1);
-  const int sw = (sg.dq >> 2) & 7;                     // (row / 16) & 7 for rows 4 dq + j
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    // column 4 dq + j of the 8 keys, two keys a word: half j & 1 of word j / 2
+    // column 4 dq + j of the granule's 8 keys, two keys a word: half j & 1 of word j / 2
     const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
     u32x4_t row;
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd)
       row[wd] = __builtin_amdgcn_perm(st.v[2 * wd + 1][j >> 1], st.v[2 * wd][j >> 1], sel);
-    half_t* r0 = &sVt[(4 * sg.dq + j) * G::VP + in_gran];
-    *reinterpret_cast<u32x2_t*>(r0 + ((g0 ^ sw) << 3)) = u32x2_t{row[0], row[1]};
-    *reinterpret_cast<u32x2_t*>(r0 + (((g0 + 1) ^ sw) << 3)) = u32x2_t{row[2], row[3]};
+    const int r = 4 * sg.dq + j;
+    *reinterpret_cast<u32x4_t*>(&sVt[r * kBk + ((sg.vq ^ swz8(r)) << 3)]) = row;
   }
 }
 
@@ -297,16 +330,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   sg.init(tid, kvh);
   const int64_t blk_stride = static_cast<int64_t>(Hkv) * kBlock * D;
   Stage<D> stg;
+  int ids_next = 0;
   if (ntiles > 0) {
     load_tile<D>(stg, sg, tile_blocks(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
+    ids_next = tile_ids_lanes(trow, 1, max_blocks, lane);
     store_tile<D>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
   }
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int key0 = kt * kBk;
     const bool more = kt + 1 < ntiles;
-    if (more)
-      load_tile<D>(stg, sg, tile_blocks(trow, kt + 1, max_blocks, num_blocks), kc, vc, blk_stride, w);
+    if (more) {
+      const TileBlocks tb = tile_blocks_from(ids_next, num_blocks);
+      ids_next = tile_ids_lanes(trow, kt + 2, max_blocks, lane);
+      load_tile<D>(stg, sg, tb, kc, vc, blk_stride, w);
+    }
     __syncthreads();  // buffer kt % 2 written; buffer (kt + 1) % 2 no longer read
     const half_t* cK = sK + (kt & 1) * G::KBUF;
     const half_t* cVt = sVt + (kt & 1) * G::VBUF;
@@ -319,15 +357,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sacc[st][ks] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int kk = 0; kk < G::DK; ++kk) {
+        half8_t a[4];
 #pragma unroll
-        for (int kk = 0; kk < G::DK; ++kk) {
-          const half8_t a =
-              *reinterpret_cast<const half8_t*>(&cK[(ks * 16 + c16) * G::KP + 32 * kk + 8 * g]);
+        for (int ks = 0; ks < 4; ++ks)
+          a[ks] = *reinterpret_cast<const half8_t*>(
+              &cK[(ks * 16 + c16) * D + (((4 * kk + g) ^ kswz<D>(ks * 16 + c16)) << 3)]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int st = 0; st < 2; ++st)
-            sacc[st][ks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[st][kk], sacc[st][ks], 0, 0, 0);
-        }
+            sacc[st][ks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], qb[st][kk], sacc[st][ks], 0, 0, 0);
       }
 
       if (key0 + kBk - 1 > P + wq_first) {  // tile crosses the diagonal of some row
@@ -350,12 +390,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         for (int ks = 0; ks < 4; ++ks)
           mt = fmaxf(mt, fmaxf(fmaxf(sacc[st][ks][0], sacc[st][ks][1]),
                                fmaxf(sacc[st][ks][2], sacc[st][ks][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        // move the running max (and rescale) only when some row's max grew by
-        // more than 2^kLazyRescale: exp2 arguments stay <= kLazyRescale
+        // move the running max (and rescale) only when some lane's scores grew
+        // past it by more than 2^kLazyRescale: exp2 arguments stay <=
+        // kLazyRescale.  The lane-local max decides; the row max over the 4
+        // lane groups is only formed when a rescale happens.
         const float grow = (mt - m[st]) * c;  // +inf on the first visible tile
         if (__ballot(grow > kLazyRescale) != 0) {
+          mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
           const float m_new = fmaxf(m[st], mt);
           const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2((m[st] - m_new) * c);
           l[st] *= corr;
@@ -389,9 +431,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         }
 #pragma unroll
         for (int dt = 0; dt < G::DT; ++dt) {
-          const int gran = (kp * 4 + g) ^ (dt & 7);  // rows 16 dt + c16: swizzle dt & 7
+          const int vr = dt * 16 + c16;
           const half8_t a =
-              *reinterpret_cast<const half8_t*>(&cVt[(dt * 16 + c16) * G::VP + (gran << 3)]);
+              *reinterpret_cast<const half8_t*>(&cVt[vr * kBk + (((kp * 4 + g) ^ swz8(vr)) << 3)]);
 #pragma unroll
           for (int st = 0; st < 2; ++st)
             o[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[st], o[st][dt], 0, 0, 0);

@@ -110,3 +110,26 @@ def test_prefill_any_finite_scale(scale):
     negative scale flips q, a zero scale gives the mean of the visible values."""
     w = workloads.custom_prefill(131, [20, 0], [40, 70], 2, 2, 128)
     check_all(PrefillCase(w), scale)
+
+
+def test_two_half_chunks_equal_one_chunk():
+    """[p1] "Mechanics of Chunked Prefill": a prompt split into chunks gives the
+    same attention as processing it in one piece.  One 512-token chunk after
+    300 cached tokens, against two 256-token calls (the second with 556 tokens
+    before it); the cache already holds every K/V row, and the causal limit
+    alone keeps each query from the rows after it."""
+    w = workloads.custom_prefill(141, [300], [512], 4, 4, 128)
+    case = PrefillCase(w)
+    one = case.run().copy()
+    halves = []
+    for lo in (0, 256):
+        q = case.q[lo:lo + 256].contiguous()
+        cu = torch.tensor([0, 256], dtype=torch.int32, device="cuda")
+        prior = torch.tensor([300 + lo], dtype=torch.int32, device="cuda")
+        out = torch.empty((256, 4, 128), dtype=torch.float32, device="cuda")
+        pa.pa_prefill_chunk(case.cache, q, cu, prior, case.tables, 256, w.scale, out)
+        torch.cuda.synchronize()
+        halves.append(out.cpu().numpy())
+    close(np.concatenate(halves).astype(np.float64), one.astype(np.float64))
+    for i in (0, 255, 256, 511):
+        close(one[i, 2], case.ref_row(0, i, 2))

@@ -14,6 +14,8 @@ Reported on one JSON line:
   fp8_decode   the same batch with an e4m3 cache
   prefix_cow   32 sequences sharing an 800-token prompt: GB/s on unique and on
                logical K/V bytes
+  prefix_cache multi-turn dialogues through the prefix cache: hit rate and
+               block-manager call times (host only)
   prefill      chunked prefill, 8 x 512-token chunks over 0..4096 cached tokens,
                causal-valid FLOPs / time against the 2.5 PFLOP/s fp16 MFMA peak
   host         block-manager call rates
@@ -260,6 +262,41 @@ def bench_prefix(pa, torch, np, workloads, reps):
             "used_blocks": stats["used_blocks"], "shared_blocks": stats["shared_blocks"]}
 
 
+def bench_prefix_cache(pa, np, workloads):
+    """Host-side prefix caching over multi-turn dialogues: every turn admits its
+    prompt with pa_alloc_prompt (reusing the conversation's cached blocks),
+    commits, appends the reply with pa_append_tokens, commits and finishes.
+    Reports the hit rate (reused prompt tokens / prompt tokens) and the block
+    manager's call times; the K/V writes are not part of this leg."""
+    d = workloads.dialogue()
+    pool = pa.pa_pool_create(d.num_blocks, 16)
+    t_prompt = t_other = 0.0
+    calls = 0
+    for t in range(len(d.turns[0])):
+        for c in range(len(d.turns)):
+            prompt, reply = d.turns[c][t]
+            s = pa.pa_seq_create(pool)
+            t0 = time.perf_counter()
+            pa.pa_alloc_prompt(pool, s, prompt)
+            t1 = time.perf_counter()
+            pa.pa_cache_commit(pool, s)
+            pa.pa_append_tokens(pool, s, reply)
+            pa.pa_cache_commit(pool, s)
+            pa.pa_seq_free(pool, s)
+            t2 = time.perf_counter()
+            t_prompt += t1 - t0
+            t_other += t2 - t1
+            calls += 1
+    st, _, _ = pa.pa_pool_state(pool)
+    return {"workload": f"dialogue: {len(d.turns)} conversations x {len(d.turns[0])} turns, first prompt "
+                        "U[200,600], replies U[20,200], messages U[10,100] tokens",
+            "prompt_tokens": st["prompt_tokens"], "hit_tokens": st["hit_tokens"],
+            "hit_rate": round(st["hit_tokens"] / max(1, st["prompt_tokens"]), 4),
+            "cached_blocks": st["cached_blocks"], "evictions": st["evictions"],
+            "alloc_prompt_us": round(1e6 * t_prompt / calls, 2),
+            "commit_append_free_us": round(1e6 * t_other / calls, 2)}
+
+
 def bench_prefill(pa, torch, np, workloads, reps):
     w = workloads.chunked_prefill()
     pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
@@ -501,6 +538,8 @@ def main():
         log("prefix sharing decode")
         res["prefix_cow"] = bench_prefix(pa, torch, np, workloads, args.steps)
         torch.cuda.empty_cache()
+        log("prefix cache (host)")
+        res["prefix_cache"] = bench_prefix_cache(pa, np, workloads)
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
     if not args.no_cpu_baseline:

@@ -84,6 +84,11 @@ typedef struct {
   int64_t live_seqs;
   int64_t tokens;         /* sum of live sequence lengths                            */
   int64_t waste_tokens;   /* sum over live sequences of blocks*block_size - length   */
+  int64_t cached_blocks;  /* blocks in the prefix cache (in use or waiting in the queue) */
+  int64_t prompt_tokens;  /* tokens admitted through pa_alloc_prompt                  */
+  int64_t hit_tokens;     /* of those, tokens served from cached blocks (hit rate =
+                             hit_tokens / prompt_tokens)                              */
+  int64_t evictions;      /* cached blocks handed out again by the free queue         */
 } pa_pool_stats;
 
 /* ---------------------------------------------------------------- host side -- */
@@ -121,6 +126,41 @@ pa_status pa_seq_create(pa_pool *pool, int32_t *seq_out);
  * blocks than needed, copy included); nothing changes on error. */
 pa_status pa_alloc_append(pa_pool *pool, int32_t seq, int32_t n_tokens,
                           int32_t *slots_out, int32_t *cow_out);
+
+/* pa_alloc_append that also records the new tokens' ids, so that the blocks
+ * they fill can enter the prefix cache (pa_cache_commit).  A sequence's ids are
+ * known only while every append supplied them: after a pa_alloc_append its later
+ * blocks are never cached.  tokens: host int32[n_tokens].  Errors as
+ * pa_alloc_append, and BAD_ARG for tokens == NULL with n_tokens > 0. */
+pa_status pa_append_tokens(pa_pool *pool, int32_t seq, const int32_t *tokens, int32_t n_tokens,
+                           int32_t *slots_out, int32_t *cow_out);
+
+/* Admit a prompt into an empty sequence, reusing cached blocks ([p2] "Deep dive",
+ * prefix-caching bullet: a block is keyed by its token ids and its parent's key,
+ * identical prefixes find the existing blocks and only full blocks are cached;
+ * [p1] "Automatic Prefix Caching (APC)", "APC Mechanics").
+ * The prompt's full blocks are looked up in order and reused up to the first
+ * miss, leaving at least the last token to compute (at most (n-1)/block_size
+ * blocks).  A reused block's ref_cnt grows by one; one waiting in the free queue
+ * is taken out of it.  Then new blocks are popped from the queue front (a popped
+ * block that was cached loses its entry: an eviction).
+ * tokens: host int32[n_tokens].  slots_out: host int32[n_tokens]; its first
+ * n_tokens - *hit_tokens_out entries receive the slots of tokens *hit_tokens_out ..
+ * n_tokens-1, the only ones whose K/V the caller must compute and write.
+ * Keys are 64-bit FNV-1a hashes chained over the parent's key; a hit also
+ * compares the stored parent key and token ids.
+ * Errors: BAD_SEQ; BAD_ARG (sequence not empty, n_tokens < 0, NULL pointers);
+ * NO_BLOCKS (reused blocks that wait in the queue count against it). */
+pa_status pa_alloc_prompt(pa_pool *pool, int32_t seq, const int32_t *tokens, int32_t n_tokens,
+                          int32_t *slots_out, int32_t *hit_tokens_out);
+
+/* Enter the sequence's full blocks whose token ids are known into the prefix
+ * cache; call it once their K/V is written (after the prefill of a prompt, or a
+ * decode step that filled a block).  A prefix already cached under another block
+ * is left as it is (one cached copy per prefix).  A cached block keeps its entry
+ * after its sequences finish, while it waits in the free queue.
+ * added_out: number of blocks entered (may be NULL).  Errors: BAD_SEQ. */
+pa_status pa_cache_commit(pa_pool *pool, int32_t seq, int32_t *added_out);
 
 /* Fork: a new sequence whose table and length equal the parent's; every shared
  * block's ref_cnt grows by one ([p1] "Virtual Memory Paging Analogy" on sharing;

@@ -25,6 +25,35 @@ Readings where the pages are silent (stated in the design notes as well):
 * copy-on-write fires only when tokens land in an existing partial last block
   whose count is above one; the last holder writes in place;
 * every call is all-or-nothing: on any error the state is unchanged.
+
+Prefix caching ([p2] "Deep dive", the prefix-caching bullet; [p1] "Automatic
+Prefix Caching (APC)", "APC Mechanics" and "Evaluating APC Hit Rates"):
+
+* a full block is identified by the token ids of the whole prefix up to its
+  end (the pages key it by its own tokens plus its parent's key, which names
+  the same prefix); only full blocks are cached;
+* a new prompt walks its full blocks from the start and reuses every block
+  whose prefix is cached, stopping at the first miss; a reused block's count
+  goes up by one ("touch"), and a reused block that sat in the free queue
+  leaves it from wherever it is;
+* freed blocks keep their cache entry while they wait in the free queue, and
+  lose it when the queue hands them out again (the queue front is the eviction
+  order);
+* the hit rate is reused prompt tokens over prompt tokens.
+
+Readings where the pages are silent:
+
+* a block enters the cache only when the caller says its K/V is written
+  (``cache_commit``), so no request can reuse a block whose K/V is still
+  being computed;
+* the last prompt token is never served from the cache (its query starts the
+  generation), so a prompt reuses at most ``(n - 1) // block_size`` blocks;
+* a sequence's tokens are known only while every append supplied them; after
+  an append without token ids its later blocks are never cached;
+* if a prefix is already cached under another block, committing an identical
+  block leaves it private (one cached copy per prefix);
+* inside ``alloc_prompt`` the reused blocks are taken first (in logical
+  order), then new blocks from the queue front.
 """
 
 from __future__ import annotations
@@ -60,6 +89,13 @@ class OraclePool:
         self.lens: Dict[int, int] = {}
         self.next_seq = 0
         self.cow_copies = 0
+        # prefix cache
+        self.tokens: Dict[int, List[int]] = {}   # known token ids per sequence
+        self.cache: Dict[Tuple[int, ...], int] = {}  # prefix -> physical block
+        self.block_key: Dict[int, Tuple[int, ...]] = {}  # physical block -> its prefix
+        self.prompt_tokens = 0
+        self.hit_tokens = 0
+        self.evictions = 0
 
     # -- sequences -------------------------------------------------------
     def seq_create(self) -> Tuple[str, int]:
@@ -67,15 +103,26 @@ class OraclePool:
         self.next_seq += 1
         self.tables[sid] = []
         self.lens[sid] = 0
+        self.tokens[sid] = []
         return Status.OK, sid
 
-    def alloc_append(self, sid: int, n: int):
+    def _take_front(self) -> int:
+        """Pop the queue front; a cached block loses its cache entry (evicted)."""
+        b = self.free.popleft()
+        key = self.block_key.pop(b, None)
+        if key is not None:
+            del self.cache[key]
+            self.evictions += 1
+        return b
+
+    def alloc_append(self, sid: int, n: int, token_ids: Optional[List[int]] = None):
         """Reserve room for ``n`` new tokens of sequence ``sid``.
 
         Returns ``(status, slots, cow)`` where ``slots[i]`` is the flat cache
         slot (physical block * block_size + offset) of token ``len + i`` and
         ``cow`` is ``(src, dst)`` when a shared partial block was copied, else
-        ``None``.
+        ``None``.  Without ``token_ids`` the sequence's later tokens are unknown
+        and its later blocks are never cached.
         """
         if sid not in self.tables:
             return Status.BAD_SEQ, [], None
@@ -97,14 +144,14 @@ class OraclePool:
         cow_pair = None
         if cow:
             src = table[-1]
-            dst = self.free.popleft()
+            dst = self._take_front()
             self.ref_cnt[src] -= 1
             self.ref_cnt[dst] = 1
             table[-1] = dst
             cow_pair = (src, dst)
             self.cow_copies += 1
         for _ in range(new_blocks):
-            b = self.free.popleft()
+            b = self._take_front()
             self.ref_cnt[b] = 1
             table.append(b)
         slots = []
@@ -112,7 +159,76 @@ class OraclePool:
             pos = length + i
             slots.append(table[pos // bs] * bs + pos % bs)
         self.lens[sid] = length + n
+        if token_ids is not None and len(self.tokens[sid]) == length:
+            self.tokens[sid].extend(int(t) for t in token_ids)
         return Status.OK, slots, cow_pair
+
+    def append_tokens(self, sid: int, token_ids: Sequence[int]):
+        """``alloc_append`` that also records the new tokens' ids."""
+        return self.alloc_append(sid, len(token_ids), token_ids=list(token_ids))
+
+    def alloc_prompt(self, sid: int, token_ids: Sequence[int]):
+        """Admit a prompt into an empty sequence, reusing cached full blocks.
+
+        Returns ``(status, slots, hit_tokens)``: the prompt's first
+        ``hit_tokens`` tokens come from cached blocks, and ``slots`` holds the
+        cache slots of the remaining tokens, in order.
+        """
+        if sid not in self.tables:
+            return Status.BAD_SEQ, [], 0
+        if self.lens[sid] != 0:
+            return Status.BAD_ARG, [], 0
+        toks = [int(t) for t in token_ids]
+        n = len(toks)
+        bs = self.block_size
+        hits = []
+        for i in range((n - 1) // bs if n > 0 else 0):
+            b = self.cache.get(tuple(toks[:bs * (i + 1)]))
+            if b is None:
+                break
+            hits.append(b)
+        new_blocks = (n + bs - 1) // bs - len(hits)
+        free_hits = sum(1 for b in hits if self.ref_cnt[b] == 0)
+        if new_blocks > len(self.free) - free_hits:
+            return Status.NO_BLOCKS, [], 0
+        table = self.tables[sid]
+        for b in hits:
+            if self.ref_cnt[b] == 0:
+                self.free.remove(b)
+            self.ref_cnt[b] += 1
+            table.append(b)
+        for _ in range(new_blocks):
+            b = self._take_front()
+            self.ref_cnt[b] = 1
+            table.append(b)
+        hit = len(hits) * bs
+        slots = [table[pos // bs] * bs + pos % bs for pos in range(hit, n)]
+        self.lens[sid] = n
+        self.tokens[sid] = toks
+        self.prompt_tokens += n
+        self.hit_tokens += hit
+        return Status.OK, slots, hit
+
+    def cache_commit(self, sid: int):
+        """Enter the sequence's full, token-known blocks into the cache (their
+        K/V is written).  Returns ``(status, newly cached blocks)``."""
+        if sid not in self.tables:
+            return Status.BAD_SEQ, 0
+        bs = self.block_size
+        toks = self.tokens[sid]
+        table = self.tables[sid]
+        added = 0
+        for i in range(len(toks) // bs):
+            key = tuple(toks[:bs * (i + 1)])
+            if key in self.cache:
+                continue
+            b = table[i]
+            if b in self.block_key:
+                continue  # already cached under its own prefix
+            self.cache[key] = b
+            self.block_key[b] = key
+            added += 1
+        return Status.OK, added
 
     def fork(self, parent: int) -> Tuple[str, int]:
         if parent not in self.tables:
@@ -121,6 +237,7 @@ class OraclePool:
         self.next_seq += 1
         self.tables[sid] = list(self.tables[parent])
         self.lens[sid] = self.lens[parent]
+        self.tokens[sid] = list(self.tokens[parent])
         for b in self.tables[sid]:
             self.ref_cnt[b] += 1
         return Status.OK, sid
@@ -134,6 +251,7 @@ class OraclePool:
                 self.free.append(b)
         del self.tables[sid]
         del self.lens[sid]
+        del self.tokens[sid]
         return Status.OK
 
     # -- export ------------------------------------------------------------
@@ -165,6 +283,10 @@ class OraclePool:
             "live_seqs": len(self.tables),
             "tokens": tokens,
             "waste_tokens": waste,
+            "cached_blocks": len(self.cache),
+            "prompt_tokens": self.prompt_tokens,
+            "hit_tokens": self.hit_tokens,
+            "evictions": self.evictions,
         }
 
     def free_order(self) -> List[int]:

@@ -62,7 +62,8 @@ class pa_kv_cache(ctypes.Structure):
 class pa_pool_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_blocks", "free_blocks", "used_blocks", "shared_blocks", "total_refs", "cow_copies",
-        "live_seqs", "tokens", "waste_tokens")]
+        "live_seqs", "tokens", "waste_tokens", "cached_blocks", "prompt_tokens", "hit_tokens",
+        "evictions")]
 
 
 # every symbol include/pa.h declares, with its ctypes signature
@@ -71,6 +72,9 @@ _SIGNATURES = {
     "pa_pool_destroy": (None, [ctypes.c_void_p]),
     "pa_seq_create": (ctypes.c_int32, [ctypes.c_void_p, _i32p]),
     "pa_alloc_append": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
+    "pa_append_tokens": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
+    "pa_alloc_prompt": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
+    "pa_cache_commit": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p]),
     "pa_fork_cow": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p]),
     "pa_seq_free": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "pa_block_tables": (ctypes.c_int32, [ctypes.c_void_p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
@@ -166,6 +170,31 @@ def pa_alloc_append(pool: Pool, seq: int, n_tokens: int) -> Tuple[np.ndarray, Op
     cow = np.full(2, -1, dtype=np.int32)
     _check(lib.pa_alloc_append(pool.handle, seq, n_tokens, _p(slots), _p(cow)))
     return slots, (None if cow[0] < 0 else (int(cow[0]), int(cow[1])))
+
+
+def pa_append_tokens(pool: Pool, seq: int, tokens) -> Tuple[np.ndarray, Optional[Tuple[int, int]]]:
+    """pa_alloc_append with the new tokens' ids recorded for prefix caching."""
+    t = _i32(tokens)
+    slots = np.empty(len(t), dtype=np.int32)
+    cow = np.full(2, -1, dtype=np.int32)
+    _check(lib.pa_append_tokens(pool.handle, seq, _p(t) if len(t) else None, len(t), _p(slots), _p(cow)))
+    return slots, (None if cow[0] < 0 else (int(cow[0]), int(cow[1])))
+
+
+def pa_alloc_prompt(pool: Pool, seq: int, tokens) -> Tuple[np.ndarray, int]:
+    """Returns (slots of the tokens to compute, hit_tokens served from the cache)."""
+    t = _i32(tokens)
+    slots = np.empty(max(len(t), 1), dtype=np.int32)
+    hit = ctypes.c_int32()
+    _check(lib.pa_alloc_prompt(pool.handle, seq, _p(t) if len(t) else None, len(t), _p(slots),
+                               ctypes.byref(hit)))
+    return slots[: len(t) - hit.value].copy(), hit.value
+
+
+def pa_cache_commit(pool: Pool, seq: int) -> int:
+    added = ctypes.c_int32()
+    _check(lib.pa_cache_commit(pool.handle, seq, ctypes.byref(added)))
+    return added.value
 
 
 def pa_fork_cow(pool: Pool, parent: int) -> int:

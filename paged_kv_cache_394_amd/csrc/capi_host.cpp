@@ -66,7 +66,34 @@ pa_status pa_alloc_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t*
                           int32_t* cow_out) {
   if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_alloc_append: pool is NULL");
   std::string err;
-  const pa::Status st = pool->impl->alloc_append(seq, n_tokens, slots_out, cow_out, &err);
+  const pa::Status st = pool->impl->alloc_append(seq, n_tokens, nullptr, slots_out, cow_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
+pa_status pa_append_tokens(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                           int32_t* slots_out, int32_t* cow_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_append_tokens: pool is NULL");
+  if (n_tokens > 0 && tokens == nullptr) return fail(PA_ERR_BAD_ARG, "pa_append_tokens: tokens is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->alloc_append(seq, n_tokens, tokens, slots_out, cow_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
+pa_status pa_alloc_prompt(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                          int32_t* slots_out, int32_t* hit_tokens_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_alloc_prompt: pool is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->alloc_prompt(seq, tokens, n_tokens, slots_out, hit_tokens_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
+pa_status pa_cache_commit(pa_pool* pool, int32_t seq, int32_t* added_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_cache_commit: pool is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->cache_commit(seq, added_out, &err);
   if (st != pa::kOk) return fail(st, err);
   return pa::ok();
 }
@@ -128,6 +155,10 @@ pa_status pa_pool_state(const pa_pool* pool, pa_pool_stats* stats_out, int32_t* 
     stats_out->live_seqs = st.live_seqs;
     stats_out->tokens = st.tokens;
     stats_out->waste_tokens = st.waste_tokens;
+    stats_out->cached_blocks = st.cached_blocks;
+    stats_out->prompt_tokens = st.prompt_tokens;
+    stats_out->hit_tokens = st.hit_tokens;
+    stats_out->evictions = st.evictions;
   }
   return pa::ok();
 }

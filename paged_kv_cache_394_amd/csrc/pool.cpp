@@ -1,6 +1,7 @@
 // Host block manager; see pool.hpp for the model and its sources.
 #include "pool.hpp"
 
+#include <cstring>
 #include <new>
 
 namespace pa {
@@ -52,12 +53,49 @@ Status BlockPool::create(int32_t num_blocks, int32_t block_size, const int32_t* 
 
 int32_t BlockPool::pop_front() {
   const int32_t b = head_;
-  head_ = next_[b];
-  if (head_ >= 0) prev_[head_] = -1; else tail_ = -1;
+  unlink(b);
+  if (!cached_.empty()) {
+    auto it = cached_.find(b);
+    if (it != cached_.end()) {  // the block's cached K/V is about to be overwritten
+      cache_.erase(it->second.key);
+      cached_.erase(it);
+      ++evictions_;
+    }
+  }
+  return b;
+}
+
+void BlockPool::unlink(int32_t b) {
+  const int32_t p = prev_[b], n = next_[b];
+  if (p >= 0) next_[p] = n; else head_ = n;
+  if (n >= 0) prev_[n] = p; else tail_ = p;
   next_[b] = prev_[b] = -1;
   in_queue_[b] = 0;
   --nfree_;
-  return b;
+}
+
+// FNV-1a (64-bit) over the parent key (8 bytes, little endian) and the block's
+// token ids (4 bytes each, little endian).
+uint64_t BlockPool::block_hash(uint64_t parent, const int32_t* ids) const {
+  uint64_t h = 14695981039346656037ull;
+  auto mix = [&h](uint8_t byte) {
+    h ^= byte;
+    h *= 1099511628211ull;
+  };
+  for (int k = 0; k < 8; ++k) mix(static_cast<uint8_t>(parent >> (8 * k)));
+  for (int32_t i = 0; i < bs_; ++i) {
+    const uint32_t t = static_cast<uint32_t>(ids[i]);
+    for (int k = 0; k < 4; ++k) mix(static_cast<uint8_t>(t >> (8 * k)));
+  }
+  return h;
+}
+
+int32_t BlockPool::lookup(uint64_t key, uint64_t parent, const int32_t* ids) const {
+  const auto it = cache_.find(key);
+  if (it == cache_.end()) return -1;
+  const Cached& c = cached_.at(it->second);
+  if (c.parent != parent || std::memcmp(c.ids.data(), ids, sizeof(int32_t) * bs_) != 0) return -1;
+  return it->second;
 }
 
 void BlockPool::push_back(int32_t b) {
@@ -83,8 +121,8 @@ Status BlockPool::seq_create(int32_t* id) {
   return kOk;
 }
 
-Status BlockPool::alloc_append(int32_t seq, int32_t n, int32_t* slots, int32_t* cow,
-                               std::string* err) {
+Status BlockPool::alloc_append(int32_t seq, int32_t n, const int32_t* tokens, int32_t* slots,
+                               int32_t* cow, std::string* err) {
   if (!live(seq)) {
     *err = "pa_alloc_append: unknown sequence";
     return kBadSeq;
@@ -119,8 +157,10 @@ Status BlockPool::alloc_append(int32_t seq, int32_t n, int32_t* slots, int32_t* 
     *err = "pa_alloc_append: not enough free blocks";
     return kNoBlocks;
   }
+  const bool record = tokens != nullptr && static_cast<int64_t>(s.tokens.size()) == len;
   try {
     s.table.reserve(static_cast<size_t>(blocks_after));
+    if (record) s.tokens.reserve(static_cast<size_t>(len + n));
   } catch (const std::bad_alloc&) {
     *err = "pa_alloc_append: out of host memory";
     return kCapacity;
@@ -152,6 +192,117 @@ Status BlockPool::alloc_append(int32_t seq, int32_t n, int32_t* slots, int32_t* 
   s.len = len + n;
   tokens_ += n;
   waste_ += (blocks_after * bs_ - s.len) - waste_before;
+  if (record) s.tokens.insert(s.tokens.end(), tokens, tokens + n);
+  return kOk;
+}
+
+Status BlockPool::alloc_prompt(int32_t seq, const int32_t* tokens, int32_t n, int32_t* slots,
+                               int32_t* hit_tokens, std::string* err) {
+  if (!live(seq)) {
+    *err = "pa_alloc_prompt: unknown sequence";
+    return kBadSeq;
+  }
+  if (n < 0 || hit_tokens == nullptr || (n > 0 && (tokens == nullptr || slots == nullptr))) {
+    *err = "pa_alloc_prompt: bad arguments";
+    return kBadArg;
+  }
+  Seq& s = seqs_[seq];
+  if (s.len != 0) {
+    *err = "pa_alloc_prompt: the sequence is not empty";
+    return kBadArg;
+  }
+  const int64_t nblk = ceil_div(n, bs_);
+  // the longest run of cached full blocks, leaving the last token to compute
+  std::vector<int32_t> hits;
+  try {
+    hits.reserve(static_cast<size_t>(nblk));
+    s.table.reserve(static_cast<size_t>(nblk));
+    s.tokens.reserve(static_cast<size_t>(n));
+  } catch (const std::bad_alloc&) {
+    *err = "pa_alloc_prompt: out of host memory";
+    return kCapacity;
+  }
+  int64_t free_hits = 0;
+  if (!cache_.empty() && n > 0) {
+    uint64_t parent = 0;
+    for (int64_t i = 0; i < (n - 1) / bs_; ++i) {
+      const int32_t* ids = tokens + i * bs_;
+      const uint64_t key = block_hash(parent, ids);
+      const int32_t b = lookup(key, parent, ids);
+      if (b < 0) break;
+      hits.push_back(b);
+      if (ref_[b] == 0) ++free_hits;
+      parent = key;
+    }
+  }
+  const int64_t new_blocks = nblk - static_cast<int64_t>(hits.size());
+  if (new_blocks > nfree_ - free_hits) {
+    *err = "pa_alloc_prompt: not enough free blocks";
+    return kNoBlocks;
+  }
+  // --- no failure past this point ---
+  for (int32_t b : hits) {
+    if (ref_[b] == 0) unlink(b);
+    if (ref_[b] == 1) ++shared_;
+    ++ref_[b];
+    ++refs_;
+    s.table.push_back(b);
+  }
+  for (int64_t j = 0; j < new_blocks; ++j) {
+    const int32_t b = pop_front();
+    ref_[b] = 1;
+    ++refs_;
+    s.table.push_back(b);
+  }
+  const int64_t hit = static_cast<int64_t>(hits.size()) * bs_;
+  for (int64_t pos = hit; pos < n; ++pos)
+    slots[pos - hit] = s.table[pos / bs_] * bs_ + static_cast<int32_t>(pos % bs_);
+  s.len = n;
+  s.tokens.assign(tokens, tokens + n);
+  tokens_ += n;
+  waste_ += nblk * bs_ - n;
+  prompt_tokens_ += n;
+  hit_tokens_ += hit;
+  *hit_tokens = static_cast<int32_t>(hit);
+  return kOk;
+}
+
+Status BlockPool::cache_commit(int32_t seq, int32_t* added, std::string* err) {
+  if (!live(seq)) {
+    *err = "pa_cache_commit: unknown sequence";
+    return kBadSeq;
+  }
+  const Seq& s = seqs_[seq];
+  const int64_t full = static_cast<int64_t>(s.tokens.size()) / bs_;
+  std::vector<int32_t> done;  // blocks inserted, for the roll-back
+  int32_t count = 0;
+  uint64_t parent = 0;
+  try {
+    for (int64_t i = 0; i < full; ++i) {
+      const int32_t* ids = s.tokens.data() + i * bs_;
+      const uint64_t key = block_hash(parent, ids);
+      const int32_t b = s.table[i];
+      // one cached copy per prefix; a block is cached under one prefix only
+      if (cache_.find(key) == cache_.end() && cached_.find(b) == cached_.end()) {
+        done.push_back(b);
+        cached_.emplace(b, Cached{key, parent, std::vector<int32_t>(ids, ids + bs_)});
+        cache_.emplace(key, b);
+        ++count;
+      }
+      parent = key;
+    }
+  } catch (const std::bad_alloc&) {
+    for (int32_t b : done) {
+      auto it = cached_.find(b);
+      if (it != cached_.end()) {
+        cache_.erase(it->second.key);
+        cached_.erase(it);
+      }
+    }
+    *err = "pa_cache_commit: out of host memory";
+    return kCapacity;
+  }
+  if (added) *added = count;
   return kOk;
 }
 
@@ -162,6 +313,7 @@ Status BlockPool::fork(int32_t parent, int32_t* child) {
   Seq c;
   try {
     c.table = seqs_[parent].table;
+    c.tokens = seqs_[parent].tokens;
     seqs_.reserve(seqs_.size() + 1);
   } catch (const std::bad_alloc&) {
     return kCapacity;
@@ -193,6 +345,7 @@ Status BlockPool::seq_free(int32_t seq) {
   tokens_ -= s.len;
   waste_ -= static_cast<int64_t>(s.table.size()) * bs_ - s.len;
   std::vector<int32_t>().swap(s.table);
+  std::vector<int32_t>().swap(s.tokens);
   s.len = 0;
   s.live = false;
   --live_seqs_;
@@ -271,6 +424,10 @@ void BlockPool::state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) cons
     st->live_seqs = live_seqs_;
     st->tokens = tokens_;
     st->waste_tokens = waste_;
+    st->cached_blocks = static_cast<int64_t>(cached_.size());
+    st->prompt_tokens = prompt_tokens_;
+    st->hit_tokens = hit_tokens_;
+    st->evictions = evictions_;
   }
   if (free_order) {
     int32_t i = 0;

@@ -9,12 +9,21 @@
 //     from the middle;
 //   * a reference count per block; a block returns to the queue at zero;
 //   * per sequence: a block table (logical -> physical) and a token count.
+// Prefix caching ([p2] "Deep dive", prefix-caching bullet; [p1] "Automatic
+// Prefix Caching (APC)"): a full block is keyed by a 64-bit chained hash of its
+// token ids and its parent block's key (FNV-1a over the parent key and the
+// block's ids); a hit is confirmed by comparing the stored parent key and ids.
+// Freed blocks keep their entry while they wait in the free queue and lose it
+// when the queue front hands them out again; a hit on a waiting block takes it
+// out of the middle of the queue.  Blocks enter the cache on cache_commit(),
+// once the caller has written their K/V.
 // Every mutating call is all-or-nothing: it validates and reserves host memory
 // first, and only then changes state.
 #pragma once
 
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 namespace pa {
@@ -29,7 +38,7 @@ enum Status : int32_t {
 
 struct PoolStats {
   int64_t num_blocks, free_blocks, used_blocks, shared_blocks, total_refs, cow_copies,
-      live_seqs, tokens, waste_tokens;
+      live_seqs, tokens, waste_tokens, cached_blocks, prompt_tokens, hit_tokens, evictions;
 };
 
 class BlockPool {
@@ -39,8 +48,18 @@ class BlockPool {
                        BlockPool** out, std::string* err);
 
   Status seq_create(int32_t* id);
-  // slots: n entries; cow: {src, dst} or {-1, -1}.
-  Status alloc_append(int32_t seq, int32_t n, int32_t* slots, int32_t* cow, std::string* err);
+  // slots: n entries; cow: {src, dst} or {-1, -1}.  tokens: the new tokens'
+  // ids (recorded for prefix caching) or nullptr (the sequence's later
+  // blocks are then never cached).
+  Status alloc_append(int32_t seq, int32_t n, const int32_t* tokens, int32_t* slots, int32_t* cow,
+                      std::string* err);
+  // Admit a prompt into an empty sequence, reusing cached full blocks; slots
+  // gets the slots of tokens hit..n-1; at most (n - 1) / block_size blocks are
+  // reused (the last token is always computed).
+  Status alloc_prompt(int32_t seq, const int32_t* tokens, int32_t n, int32_t* slots,
+                      int32_t* hit_tokens, std::string* err);
+  // Enter the sequence's full, token-known blocks into the prefix cache.
+  Status cache_commit(int32_t seq, int32_t* added, std::string* err);
   Status fork(int32_t parent, int32_t* child);
   Status seq_free(int32_t seq);
   Status block_tables(const int32_t* seqs, int32_t n, int32_t max_blocks, int32_t* tables,
@@ -59,13 +78,22 @@ class BlockPool {
   bool live(int32_t seq) const {
     return seq >= 0 && seq < static_cast<int32_t>(seqs_.size()) && seqs_[seq].live;
   }
-  int32_t pop_front();
+  int32_t pop_front();  // evicts the block's cache entry, if any
   void push_back(int32_t b);
+  void unlink(int32_t b);  // remove from the middle of the free queue
+  uint64_t block_hash(uint64_t parent, const int32_t* ids) const;
+  // cached block for this (parent key, ids), or -1
+  int32_t lookup(uint64_t key, uint64_t parent, const int32_t* ids) const;
 
   struct Seq {
     std::vector<int32_t> table;
+    std::vector<int32_t> tokens;  // ids of the leading tokens, while every append gave them
     int64_t len = 0;
     bool live = false;
+  };
+  struct Cached {
+    uint64_t key, parent;
+    std::vector<int32_t> ids;
   };
 
   int32_t n_, bs_;
@@ -76,6 +104,9 @@ class BlockPool {
   std::vector<int32_t> ref_;
   std::vector<Seq> seqs_;  // indexed by id; ids are never reused
   int64_t live_seqs_ = 0, tokens_ = 0, waste_ = 0, cow_copies_ = 0, shared_ = 0, refs_ = 0;
+  std::unordered_map<uint64_t, int32_t> cache_;   // key -> block
+  std::unordered_map<int32_t, Cached> cached_;    // block -> its entry
+  int64_t prompt_tokens_ = 0, hit_tokens_ = 0, evictions_ = 0;
 };
 
 }  // namespace pa

@@ -58,6 +58,41 @@ class Pair:
             assert slots.tolist() == oslots and cow == ocow
         return st_, slots, cow
 
+    def prompt(self, s, toks):
+        try:
+            slots, hit = pa.pa_alloc_prompt(self.lib, s, toks)
+            lib_st = Status.OK
+        except pa.PaError as e:
+            lib_st, slots, hit = e.name, None, None
+        st_, oslots, ohit = self.orc.alloc_prompt(s, toks)
+        assert lib_st == st_
+        if st_ == Status.OK:
+            assert slots.tolist() == oslots and hit == ohit
+        return st_, hit
+
+    def append_tokens(self, s, toks):
+        try:
+            slots, cow = pa.pa_append_tokens(self.lib, s, toks)
+            lib_st = Status.OK
+        except pa.PaError as e:
+            lib_st, slots, cow = e.name, None, None
+        st_, oslots, ocow = self.orc.append_tokens(s, toks)
+        assert lib_st == st_
+        if st_ == Status.OK:
+            assert slots.tolist() == oslots and cow == ocow
+        return st_
+
+    def commit(self, s):
+        try:
+            added = pa.pa_cache_commit(self.lib, s)
+            lib_st = Status.OK
+        except pa.PaError as e:
+            lib_st, added = e.name, None
+        st_, oadded = self.orc.cache_commit(s)
+        assert lib_st == st_
+        if st_ == Status.OK:
+            assert added == oadded
+
     def fork(self, s):
         try:
             c = pa.pa_fork_cow(self.lib, s)
@@ -205,3 +240,60 @@ def test_random_op_sequences_match_oracle(ops, n, bs, seed):
         else:
             p.free(1000 + i)
         p.check()
+
+
+apc_ops = st.lists(st.tuples(st.sampled_from(["new", "prompt", "append_tokens", "append", "commit",
+                                              "fork", "free"]),
+                             st.integers(0, 50), st.integers(0, 70), st.integers(0, 3)),
+                   min_size=1, max_size=60)
+
+
+@settings(max_examples=200, deadline=None)
+@given(ops=apc_ops, n=st.integers(2, 24), bs=st.sampled_from([1, 3, 16]), seed=st.integers(0, 999))
+def test_prefix_cache_ops_match_oracle(ops, n, bs, seed):
+    """Prompts drawn from three shared bases over a 3-token vocabulary, so
+    prefixes repeat, hit, diverge, get evicted and come back."""
+    r = random.Random(seed)
+    order = list(range(n))
+    r.shuffle(order)
+    p = Pair(n, bs, order)
+    bases = [[r.randrange(3) for _ in range(80)] for _ in range(3)]
+    live = []
+    for op, i, k, which in ops:
+        if op == "new" or not live:
+            live.append(p.create())
+        elif op == "prompt":
+            s = p.create()
+            toks = bases[which % 3][:k] + [r.randrange(3) for _ in range(i % 7)]
+            p.prompt(s, toks)
+            live.append(s)
+        elif op == "append_tokens":
+            p.append_tokens(live[i % len(live)], [r.randrange(3) for _ in range(k % 20)])
+        elif op == "append":
+            p.append(live[i % len(live)], k % 20)
+        elif op == "commit":
+            p.commit(live[i % len(live)])
+        elif op == "fork":
+            live.append(p.fork(live[i % len(live)]))
+        else:
+            p.free(live.pop(i % len(live)))
+        p.check()
+
+
+def test_prefix_cache_errors_and_hit_rate():
+    p = Pair(8, 16)
+    a = p.create()
+    toks = list(range(40))
+    assert p.prompt(a, toks) == (Status.OK, 0)
+    p.commit(a)
+    assert p.prompt(a, toks)[0] == Status.BAD_ARG          # not empty
+    assert p.prompt(123, toks)[0] == Status.BAD_SEQ
+    b = p.create()
+    assert p.prompt(b, toks) == (Status.OK, 32)
+    p.check()
+    stats, _, _ = pa.pa_pool_state(p.lib)
+    assert stats["hit_tokens"] / stats["prompt_tokens"] == 32 / 80
+    c = p.create()
+    assert pa.lib.pa_alloc_prompt(p.lib.handle, c, None, 5, None, None) == pa.PA_ERR_BAD_ARG
+    assert pa.lib.pa_append_tokens(p.lib.handle, c, None, 5, None, None) == pa.PA_ERR_BAD_ARG
+    assert pa.lib.pa_cache_commit(p.lib.handle, 999, None) == pa.PA_ERR_BAD_SEQ

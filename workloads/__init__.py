@@ -255,3 +255,70 @@ WORKLOADS = {
     "prefix_cow": prefix_cow,
     "chunked_prefill": chunked_prefill,
 }
+
+
+@dataclass
+class Dialogue:
+    """Multi-turn conversations for prefix caching ([p1] "Automatic Prefix
+    Caching (APC)": each turn's prompt starts with the conversation so far).
+
+    ``turns[c][t]`` is ``(prompt, reply)``: token-id lists; the prompt of turn
+    t + 1 is the prompt of turn t, its reply, then a new user message.  K/V rows
+    depend only on the token id and its position (an embedding-plus-position
+    stand-in for a model), so identical prefixes carry identical K/V, as the
+    pages require of a reusable block; ``kv(tokens, lo, hi)`` gives rows lo..hi-1.
+    """
+    seed: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    vocab: int
+    turns: List[List[Tuple[List[int], List[int]]]]
+    num_blocks: int
+    _tok_k: np.ndarray = field(repr=False, default=None)
+    _tok_v: np.ndarray = field(repr=False, default=None)
+    _pos_k: np.ndarray = field(repr=False, default=None)
+    _pos_v: np.ndarray = field(repr=False, default=None)
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.head_dim))
+
+    def kv(self, tokens, lo: int, hi: int) -> Tuple[np.ndarray, np.ndarray]:
+        ids = np.asarray(tokens[lo:hi], dtype=np.int64)
+        pos = np.arange(lo, hi)
+        k = (self._tok_k[ids] + self._pos_k[pos]).astype(np.float16)
+        v = (self._tok_v[ids] + self._pos_v[pos]).astype(np.float16)
+        return k, v
+
+    def query(self, c: int, t: int) -> np.ndarray:
+        rng = np.random.default_rng((self.seed, 1000 + c, t))
+        return _draw(rng, (self.num_heads, self.head_dim), "normal")
+
+
+def dialogue(seed: int = 1006, conversations: int = 16, turns: int = 4, num_heads: int = 8,
+             num_kv_heads: int = 8, head_dim: int = 128, vocab: int = 512,
+             first=(200, 600), reply=(20, 200), message=(10, 100)) -> Dialogue:
+    """``conversations`` dialogues of ``turns`` turns: first prompts U[first],
+    replies U[reply], user messages U[message] tokens (inclusive bounds)."""
+    rng = np.random.default_rng(seed)
+    convs = []
+    max_len = 0
+    for _ in range(conversations):
+        prompt = rng.integers(0, vocab, size=int(rng.integers(first[0], first[1] + 1))).tolist()
+        conv = []
+        for t in range(turns):
+            rep = rng.integers(0, vocab, size=int(rng.integers(reply[0], reply[1] + 1))).tolist()
+            conv.append((list(prompt), rep))
+            max_len = max(max_len, len(prompt) + len(rep))
+            msg = rng.integers(0, vocab, size=int(rng.integers(message[0], message[1] + 1))).tolist()
+            prompt = prompt + rep + msg
+        convs.append(conv)
+    tok_k = _draw(rng, (vocab, num_kv_heads, head_dim), "normal") * np.float32(0.7)
+    tok_v = _draw(rng, (vocab, num_kv_heads, head_dim), "normal")
+    pos_k = _draw(rng, (max_len + 1, num_kv_heads, head_dim), "normal") * np.float32(0.7)
+    pos_v = _draw(rng, (max_len + 1, num_kv_heads, head_dim), "normal") * np.float32(0.1)
+    # room for every conversation's longest turn at once, plus slack for cached blocks
+    need = sum(_ceil_div(len(c[-1][0]) + len(c[-1][1]), BLOCK_SIZE) for c in convs)
+    return Dialogue(seed, num_heads, num_kv_heads, head_dim, vocab, convs, int(need * 2 + 16),
+                    tok_k, tok_v, pos_k, pos_v)

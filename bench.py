@@ -16,6 +16,8 @@ Reported on one JSON line:
                logical K/V bytes
   prefix_cache multi-turn dialogues through the prefix cache: hit rate and
                block-manager call times (host only)
+  preemption   one 2048-token sequence swapped to pinned host memory and back
+               (PCIe GB/s), against its attention-side recomputation
   prefill      chunked prefill, 8 x 512-token chunks over 0..4096 cached tokens,
                causal-valid FLOPs / time against the 2.5 PFLOP/s fp16 MFMA peak
   host         block-manager call rates
@@ -297,6 +299,64 @@ def bench_prefix_cache(pa, np, workloads):
             "commit_append_free_us": round(1e6 * t_other / calls, 2)}
 
 
+def bench_preemption(pa, torch, np, workloads, reps=10):
+    """Preemption of one 2048-token sequence at the 13B shape (128 blocks, 40 MiB
+    of fp16 K/V per layer): swap out to pinned host memory and back in
+    (pa_swap_out / pa_swap_in + pa_swap_blocks), against the attention-side
+    part of recomputing it (K/V write + chunked prefill, 4 x 512 tokens) for one
+    layer.  The model's own projections, which recomputation also repeats, are
+    not part of this library and not timed."""
+    L, H, D = 2048, 40, 128
+    nblk = L // 16
+    pool = pa.pa_pool_create(nblk + 16, 16)
+    cache = pa.KvCache(nblk + 16, H, D)
+    rng = np.random.default_rng(1007)
+    k = torch.from_numpy(rng.standard_normal((L, H, D), dtype=np.float32).astype(np.float16)).cuda()
+    v = torch.from_numpy(rng.standard_normal((L, H, D), dtype=np.float32).astype(np.float16)).cuda()
+    q = torch.from_numpy(rng.standard_normal((L, H, D), dtype=np.float32).astype(np.float16)).cuda()
+    s = pa.pa_seq_create(pool)
+    slots, _ = pa.pa_alloc_append(pool, s, L)
+    pa.pa_write_kv(cache, k, v, torch.from_numpy(slots).cuda())
+    host_k = torch.empty((nblk, H, 16, D), dtype=torch.float16, pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    pa.pa_swap_space(pool, nblk)
+
+    def swap_cycle():
+        t0 = time.perf_counter()
+        pa.pa_swap_blocks(cache, host_k, host_v, pa.pa_swap_out(pool, s), 0)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        pa.pa_swap_blocks(cache, host_k, host_v, pa.pa_swap_in(pool, s), 1)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
+
+    for _ in range(3):
+        swap_cycle()
+    outs, ins = zip(*[swap_cycle() for _ in range(reps)])
+    t_out, t_in = sorted(outs)[reps // 2], sorted(ins)[reps // 2]
+    nbytes = 2 * nblk * H * 16 * D * 2
+    tables, _ = pa.pa_block_tables(pool, [s], nblk)
+    tables = torch.from_numpy(tables).cuda()
+    out = torch.empty((512, H, D), dtype=torch.float32, device="cuda")
+    cu = torch.tensor([0, 512], dtype=torch.int32, device="cuda")
+    priors = [torch.tensor([c * 512], dtype=torch.int32, device="cuda") for c in range(4)]
+    slots_d = torch.from_numpy(slots).cuda()
+    scale = 1.0 / np.sqrt(D)
+
+    def recompute():
+        pa.pa_write_kv(cache, k, v, slots_d)
+        for c in range(4):
+            pa.pa_prefill_chunk(cache, q[c * 512:(c + 1) * 512], cu, priors[c], tables, 512, scale, out)
+
+    mean, _ = time_events(torch, recompute, reps)
+    return {"workload": "one 2048-token sequence, 40 KV heads x 128, fp16: 128 blocks, "
+                        f"{nbytes / 2**20:.0f} MiB of K/V per layer",
+            "swap_out_ms": round(1e3 * t_out, 3), "swap_in_ms": round(1e3 * t_in, 3),
+            "swap_out_gbs": round(nbytes / t_out / 1e9, 2), "swap_in_gbs": round(nbytes / t_in / 1e9, 2),
+            "recompute_attention_ms_per_layer": round(mean, 3)}
+
+
 def bench_prefill(pa, torch, np, workloads, reps):
     w = workloads.chunked_prefill()
     pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
@@ -540,6 +600,9 @@ def main():
         torch.cuda.empty_cache()
         log("prefix cache (host)")
         res["prefix_cache"] = bench_prefix_cache(pa, np, workloads)
+        log("preemption: swap vs recompute")
+        res["preemption"] = bench_preemption(pa, torch, np, workloads)
+        torch.cuda.empty_cache()
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
     if not args.no_cpu_baseline:

@@ -89,6 +89,9 @@ typedef struct {
   int64_t hit_tokens;     /* of those, tokens served from cached blocks (hit rate =
                              hit_tokens / prompt_tokens)                              */
   int64_t evictions;      /* cached blocks handed out again by the free queue         */
+  int64_t host_blocks;    /* size of the host swap space (pa_swap_space)              */
+  int64_t host_free_blocks;
+  int64_t swapped_seqs;   /* live sequences whose blocks are in host memory           */
 } pa_pool_stats;
 
 /* ---------------------------------------------------------------- host side -- */
@@ -162,6 +165,36 @@ pa_status pa_alloc_prompt(pa_pool *pool, int32_t seq, const int32_t *tokens, int
  * added_out: number of blocks entered (may be NULL).  Errors: BAD_SEQ. */
 pa_status pa_cache_commit(pa_pool *pool, int32_t seq, int32_t *added_out);
 
+/* Preemption by swapping ([p3] "What happens when the GPU runs out of KV
+ * blocks?": copy a sequence's blocks to CPU RAM over PCIe and back when it is
+ * rescheduled; the other strategy, recomputation, is pa_seq_free followed by a
+ * new admission and prefill).  The pool keeps a host swap space of
+ * num_host_blocks block ids with its own FIFO free queue (ids 0..n-1 at first);
+ * the caller owns the host memory those ids index (pa_swap_blocks).
+ * pa_swap_space sets its size; allowed only while no sequence is swapped out.
+ * Errors: BAD_ARG (negative size, sequences swapped out). */
+pa_status pa_swap_space(pa_pool *pool, int32_t num_host_blocks);
+
+/* Swap a sequence out: for each block in logical order take a host block from
+ * the front of the host queue, emit the pair {device, host}, and drop the
+ * sequence's reference to the device block (which returns to the back of the
+ * device free queue at ref_cnt 0, keeping any prefix-cache entry).  The
+ * sequence keeps its length and token ids; until pa_swap_in it cannot be
+ * appended to, forked, committed or exported (BAD_ARG).  pairs_out: host
+ * int32[cap][2]; *n_out: number of pairs (= its blocks).  The caller must issue
+ * the device-to-host copies (pa_swap_blocks, direction 0) on its stream before
+ * any work that may write the released blocks.
+ * Errors: BAD_SEQ; BAD_ARG (already swapped out, NULL); CAPACITY (cap too small);
+ * NO_BLOCKS (host queue too short). */
+pa_status pa_swap_out(pa_pool *pool, int32_t seq, int32_t *pairs_out, int32_t cap, int32_t *n_out);
+
+/* Swap a sequence back in: for each host block in logical order pop a device
+ * block from the free queue front (ref_cnt 1), emit {host, device}, and return
+ * the host block to the back of the host queue.  The caller issues the
+ * host-to-device copies (pa_swap_blocks, direction 1) before using the sequence.
+ * Errors: BAD_SEQ; BAD_ARG (not swapped out, NULL); CAPACITY; NO_BLOCKS. */
+pa_status pa_swap_in(pa_pool *pool, int32_t seq, int32_t *pairs_out, int32_t cap, int32_t *n_out);
+
 /* Fork: a new sequence whose table and length equal the parent's; every shared
  * block's ref_cnt grows by one ([p1] "Virtual Memory Paging Analogy" on sharing;
  * [p3] copy-on-write section: one copy of the prompt KV, like fork()).
@@ -219,6 +252,19 @@ pa_status pa_write_kv(const pa_kv_cache *cache, const void *k_new, const void *v
 /* Bytes of device workspace pa_decode needs for this shape (split-K partials). */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len);
+
+/* Copy whole blocks between the device cache and caller-owned host memory, for
+ * pa_swap_out / pa_swap_in.  host_k / host_v: host buffers of num_host_blocks
+ * blocks each, in the cache's layout [block][num_kv_heads][block_size][head_dim]
+ * (pinned memory from hipHostMalloc for asynchronous copies).  pairs_host:
+ * host int32[n_pairs][2] as emitted: {device, host} for direction 0
+ * (device -> host), {host, device} for direction 1 (host -> device).  Runs of
+ * consecutive ids are merged into one copy per cache; copies are enqueued on
+ * hip_stream with hipMemcpyAsync.  Errors: BAD_ARG (ids out of range, NULL,
+ * bad direction), HIP. */
+pa_status pa_swap_blocks(const pa_kv_cache *cache, void *host_k, void *host_v,
+                         int32_t num_host_blocks, const int32_t *pairs_host, int32_t n_pairs,
+                         int32_t direction, void *hip_stream);
 
 /* Decode attention: one query per sequence over its paged context ([p1]
  * "PagedAttention Mechanism": look the physical blocks up in the block table,

@@ -54,6 +54,21 @@ Readings where the pages are silent:
   block leaves it private (one cached copy per prefix);
 * inside ``alloc_prompt`` the reused blocks are taken first (in logical
   order), then new blocks from the queue front.
+
+Preemption by swapping ([p3] "What happens when the GPU runs out of KV
+blocks?": copy the evicted blocks to CPU RAM, copy them back when the sequence
+is rescheduled):
+
+* host blocks form a second pool with its own first-in first-out queue;
+* swapping out walks the table in logical order, takes a host block from the
+  host queue front for each block and drops the sequence's reference to the
+  device block (back of the device queue at zero);
+* swapping in walks the host table in logical order, takes a device block from
+  the queue front for each and returns the host block to the back of the host
+  queue;
+* a swapped-out sequence keeps its length and tokens but cannot grow, fork,
+  commit or be exported until it is swapped in; its tokens count neither in
+  ``tokens`` nor in ``waste_tokens`` (those describe device memory).
 """
 
 from __future__ import annotations
@@ -96,6 +111,10 @@ class OraclePool:
         self.prompt_tokens = 0
         self.hit_tokens = 0
         self.evictions = 0
+        # swap space
+        self.host_n = 0
+        self.host_free = collections.deque()
+        self.swapped = set()
 
     # -- sequences -------------------------------------------------------
     def seq_create(self) -> Tuple[str, int]:
@@ -126,7 +145,7 @@ class OraclePool:
         """
         if sid not in self.tables:
             return Status.BAD_SEQ, [], None
-        if n < 0:
+        if n < 0 or sid in self.swapped:
             return Status.BAD_ARG, [], None
         bs = self.block_size
         table = self.tables[sid]
@@ -176,7 +195,7 @@ class OraclePool:
         """
         if sid not in self.tables:
             return Status.BAD_SEQ, [], 0
-        if self.lens[sid] != 0:
+        if self.lens[sid] != 0 or sid in self.swapped:
             return Status.BAD_ARG, [], 0
         toks = [int(t) for t in token_ids]
         n = len(toks)
@@ -214,6 +233,8 @@ class OraclePool:
         K/V is written).  Returns ``(status, newly cached blocks)``."""
         if sid not in self.tables:
             return Status.BAD_SEQ, 0
+        if sid in self.swapped:
+            return Status.BAD_ARG, 0
         bs = self.block_size
         toks = self.tokens[sid]
         table = self.tables[sid]
@@ -233,6 +254,8 @@ class OraclePool:
     def fork(self, parent: int) -> Tuple[str, int]:
         if parent not in self.tables:
             return Status.BAD_SEQ, -1
+        if parent in self.swapped:
+            return Status.BAD_ARG, -1
         sid = self.next_seq
         self.next_seq += 1
         self.tables[sid] = list(self.tables[parent])
@@ -245,10 +268,14 @@ class OraclePool:
     def seq_free(self, sid: int) -> str:
         if sid not in self.tables:
             return Status.BAD_SEQ
-        for b in self.tables[sid]:
-            self.ref_cnt[b] -= 1
-            if self.ref_cnt[b] == 0:
-                self.free.append(b)
+        if sid in self.swapped:
+            self.host_free.extend(self.tables[sid])
+            self.swapped.discard(sid)
+        else:
+            for b in self.tables[sid]:
+                self.ref_cnt[b] -= 1
+                if self.ref_cnt[b] == 0:
+                    self.free.append(b)
         del self.tables[sid]
         del self.lens[sid]
         del self.tokens[sid]
@@ -260,6 +287,8 @@ class OraclePool:
         for s in sids:
             if s not in self.tables:
                 return Status.BAD_SEQ, None, None
+            if s in self.swapped:
+                return Status.BAD_ARG, None, None
             if len(self.tables[s]) > max_blocks:
                 return Status.CAPACITY, None, None
         rows, lens = [], []
@@ -269,10 +298,58 @@ class OraclePool:
             lens.append(self.lens[s])
         return Status.OK, rows, lens
 
+    # -- swapping ----------------------------------------------------------
+    def set_swap_space(self, n: int) -> str:
+        if n < 0 or self.swapped:
+            return Status.BAD_ARG
+        self.host_n = n
+        self.host_free = collections.deque(range(n))
+        return Status.OK
+
+    def swap_out(self, sid: int):
+        """Returns ``(status, [(device, host), ...])``."""
+        if sid not in self.tables:
+            return Status.BAD_SEQ, []
+        if sid in self.swapped:
+            return Status.BAD_ARG, []
+        table = self.tables[sid]
+        if len(table) > len(self.host_free):
+            return Status.NO_BLOCKS, []
+        pairs = []
+        for i, b in enumerate(table):
+            h = self.host_free.popleft()
+            pairs.append((b, h))
+            self.ref_cnt[b] -= 1
+            if self.ref_cnt[b] == 0:
+                self.free.append(b)
+            table[i] = h
+        self.swapped.add(sid)
+        return Status.OK, pairs
+
+    def swap_in(self, sid: int):
+        """Returns ``(status, [(host, device), ...])``."""
+        if sid not in self.tables:
+            return Status.BAD_SEQ, []
+        if sid not in self.swapped:
+            return Status.BAD_ARG, []
+        table = self.tables[sid]
+        if len(table) > len(self.free):
+            return Status.NO_BLOCKS, []
+        pairs = []
+        for i, h in enumerate(table):
+            b = self._take_front()
+            self.ref_cnt[b] = 1
+            pairs.append((h, b))
+            self.host_free.append(h)
+            table[i] = b
+        self.swapped.discard(sid)
+        return Status.OK, pairs
+
     def stats(self) -> Dict[str, int]:
         free = len(self.free)
-        tokens = sum(self.lens.values())
-        waste = sum(len(self.tables[s]) * self.block_size - self.lens[s] for s in self.tables)
+        dev = [s for s in self.tables if s not in self.swapped]
+        tokens = sum(self.lens[s] for s in dev)
+        waste = sum(len(self.tables[s]) * self.block_size - self.lens[s] for s in dev)
         return {
             "num_blocks": self.num_blocks,
             "free_blocks": free,
@@ -287,6 +364,9 @@ class OraclePool:
             "prompt_tokens": self.prompt_tokens,
             "hit_tokens": self.hit_tokens,
             "evictions": self.evictions,
+            "host_blocks": self.host_n,
+            "host_free_blocks": len(self.host_free),
+            "swapped_seqs": len(self.swapped),
         }
 
     def free_order(self) -> List[int]:

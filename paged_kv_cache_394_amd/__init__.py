@@ -63,7 +63,7 @@ class pa_pool_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_blocks", "free_blocks", "used_blocks", "shared_blocks", "total_refs", "cow_copies",
         "live_seqs", "tokens", "waste_tokens", "cached_blocks", "prompt_tokens", "hit_tokens",
-        "evictions")]
+        "evictions", "host_blocks", "host_free_blocks", "swapped_seqs")]
 
 
 # every symbol include/pa.h declares, with its ctypes signature
@@ -75,6 +75,12 @@ _SIGNATURES = {
     "pa_append_tokens": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
     "pa_alloc_prompt": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
     "pa_cache_commit": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p]),
+    "pa_swap_space": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
+    "pa_swap_out": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p]),
+    "pa_swap_in": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p]),
+    "pa_swap_blocks": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p]),
     "pa_fork_cow": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p]),
     "pa_seq_free": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "pa_block_tables": (ctypes.c_int32, [ctypes.c_void_p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
@@ -195,6 +201,28 @@ def pa_cache_commit(pool: Pool, seq: int) -> int:
     added = ctypes.c_int32()
     _check(lib.pa_cache_commit(pool.handle, seq, ctypes.byref(added)))
     return added.value
+
+
+def pa_swap_space(pool: Pool, num_host_blocks: int) -> None:
+    _check(lib.pa_swap_space(pool.handle, num_host_blocks))
+
+
+def _swap(fn, pool: Pool, seq: int) -> np.ndarray:
+    n = ctypes.c_int32()
+    cap = max(1, pa_seq_table(pool, seq)[0].size)
+    pairs = np.empty((cap, 2), dtype=np.int32)
+    _check(fn(pool.handle, seq, _p(pairs), cap, ctypes.byref(n)))
+    return pairs[: n.value].copy()
+
+
+def pa_swap_out(pool: Pool, seq: int) -> np.ndarray:
+    """Returns the {device, host} block pairs to copy, int32[n][2]."""
+    return _swap(lib.pa_swap_out, pool, seq)
+
+
+def pa_swap_in(pool: Pool, seq: int) -> np.ndarray:
+    """Returns the {host, device} block pairs to copy, int32[n][2]."""
+    return _swap(lib.pa_swap_in, pool, seq)
 
 
 def pa_fork_cow(pool: Pool, parent: int) -> int:
@@ -328,6 +356,18 @@ def pa_prefill_chunk(cache: KvCache, q: torch.Tensor, cu_q: torch.Tensor, prior:
                                 _dev(cu_q, torch.int32), _dev(prior, torch.int32),
                                 _dev(tables, torch.int32), B, tables.shape[1], max_chunk, scale,
                                 _dev(out, torch.float32), _stream(stream)))
+
+
+def pa_swap_blocks(cache: "KvCache", host_k: torch.Tensor, host_v: torch.Tensor, pairs,
+                   direction: int, stream=None) -> None:
+    """host_k / host_v: pinned CPU tensors [num_host_blocks][Hkv][bs][D] of the
+    cache dtype; pairs as returned by pa_swap_out (direction 0) or pa_swap_in (1)."""
+    pr = _i32(pairs).reshape(-1, 2)
+    if host_k.device.type != "cpu" or host_v.device.type != "cpu" or host_k.shape != host_v.shape:
+        raise PaError(PA_ERR_BAD_ARG, "host_k / host_v must be CPU tensors of one shape")
+    _check(lib.pa_swap_blocks(ctypes.byref(cache.desc), host_k.data_ptr(), host_v.data_ptr(),
+                              int(host_k.shape[0]), _p(pr) if len(pr) else None, len(pr), direction,
+                              _stream(stream)))
 
 
 def version() -> str:

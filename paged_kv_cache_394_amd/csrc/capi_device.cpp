@@ -143,4 +143,48 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t num_
                     fn);
 }
 
+pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v,
+                         int32_t num_host_blocks, const int32_t* pairs_host, int32_t n_pairs,
+                         int32_t direction, void* hip_stream) {
+  const char* fn = "pa_swap_blocks";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  if (n_pairs < 0 || num_host_blocks < 0 || (direction != 0 && direction != 1))
+    return fail(PA_ERR_BAD_ARG, "pa_swap_blocks: bad count or direction");
+  if (n_pairs == 0) return pa::ok();
+  if (pairs_host == nullptr || host_k == nullptr || host_v == nullptr)
+    return fail(PA_ERR_BAD_ARG, "pa_swap_blocks: NULL pointer");
+  for (int32_t i = 0; i < n_pairs; ++i) {
+    const int32_t dev = pairs_host[2 * i + (direction == 0 ? 0 : 1)];
+    const int32_t host = pairs_host[2 * i + (direction == 0 ? 1 : 0)];
+    if (dev < 0 || dev >= d.num_blocks || host < 0 || host >= num_host_blocks)
+      return fail(PA_ERR_BAD_ARG, "pa_swap_blocks: block id out of range");
+  }
+  const size_t block_bytes =
+      static_cast<size_t>(d.num_kv_heads) * d.block_size * d.head_dim * (d.fp8 ? 1 : 2);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  // runs of consecutive device and host ids go in one copy per cache
+  int32_t i = 0;
+  while (i < n_pairs) {
+    const int32_t dev0 = pairs_host[2 * i + (direction == 0 ? 0 : 1)];
+    const int32_t host0 = pairs_host[2 * i + (direction == 0 ? 1 : 0)];
+    int32_t run = 1;
+    while (i + run < n_pairs &&
+           pairs_host[2 * (i + run) + (direction == 0 ? 0 : 1)] == dev0 + run &&
+           pairs_host[2 * (i + run) + (direction == 0 ? 1 : 0)] == host0 + run)
+      ++run;
+    const size_t bytes = block_bytes * run;
+    for (int which = 0; which < 2; ++which) {
+      char* dev_base = static_cast<char*>(which == 0 ? d.k : d.v) + block_bytes * dev0;
+      char* host_base = static_cast<char*>(which == 0 ? host_k : host_v) + block_bytes * host0;
+      const hipError_t e =
+          direction == 0 ? hipMemcpyAsync(host_base, dev_base, bytes, hipMemcpyDeviceToHost, s)
+                         : hipMemcpyAsync(dev_base, host_base, bytes, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_status(e, fn);
+    }
+    i += run;
+  }
+  return pa::ok();
+}
+
 }  // extern "C"

@@ -90,6 +90,30 @@ pa_status pa_alloc_prompt(pa_pool* pool, int32_t seq, const int32_t* tokens, int
   return pa::ok();
 }
 
+pa_status pa_swap_space(pa_pool* pool, int32_t num_host_blocks) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_swap_space: pool is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->set_swap_space(num_host_blocks, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
+pa_status pa_swap_out(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_swap_out: pool is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->swap_out(seq, pairs_out, cap, n_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
+pa_status pa_swap_in(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_swap_in: pool is NULL");
+  std::string err;
+  const pa::Status st = pool->impl->swap_in(seq, pairs_out, cap, n_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
 pa_status pa_cache_commit(pa_pool* pool, int32_t seq, int32_t* added_out) {
   if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_cache_commit: pool is NULL");
   std::string err;
@@ -159,6 +183,9 @@ pa_status pa_pool_state(const pa_pool* pool, pa_pool_stats* stats_out, int32_t* 
     stats_out->prompt_tokens = st.prompt_tokens;
     stats_out->hit_tokens = st.hit_tokens;
     stats_out->evictions = st.evictions;
+    stats_out->host_blocks = st.host_blocks;
+    stats_out->host_free_blocks = st.host_free_blocks;
+    stats_out->swapped_seqs = st.swapped_seqs;
   }
   return pa::ok();
 }

@@ -136,6 +136,10 @@ Status BlockPool::alloc_append(int32_t seq, int32_t n, const int32_t* tokens, in
     return kBadArg;
   }
   Seq& s = seqs_[seq];
+  if (s.swapped) {
+    *err = "pa_alloc_append: the sequence is swapped out";
+    return kBadArg;
+  }
   if (cow != nullptr) cow[0] = cow[1] = -1;
   if (n == 0) return kOk;
   const int64_t len = s.len;
@@ -207,7 +211,7 @@ Status BlockPool::alloc_prompt(int32_t seq, const int32_t* tokens, int32_t n, in
     return kBadArg;
   }
   Seq& s = seqs_[seq];
-  if (s.len != 0) {
+  if (s.len != 0 || s.swapped) {
     *err = "pa_alloc_prompt: the sequence is not empty";
     return kBadArg;
   }
@@ -273,6 +277,10 @@ Status BlockPool::cache_commit(int32_t seq, int32_t* added, std::string* err) {
     return kBadSeq;
   }
   const Seq& s = seqs_[seq];
+  if (s.swapped) {
+    *err = "pa_cache_commit: the sequence is swapped out";
+    return kBadArg;
+  }
   const int64_t full = static_cast<int64_t>(s.tokens.size()) / bs_;
   std::vector<int32_t> done;  // blocks inserted, for the roll-back
   int32_t count = 0;
@@ -308,7 +316,7 @@ Status BlockPool::cache_commit(int32_t seq, int32_t* added, std::string* err) {
 
 Status BlockPool::fork(int32_t parent, int32_t* child) {
   if (!live(parent)) return kBadSeq;
-  if (child == nullptr) return kBadArg;
+  if (child == nullptr || seqs_[parent].swapped) return kBadArg;
   if (seqs_.size() >= static_cast<size_t>(INT32_MAX)) return kCapacity;
   Seq c;
   try {
@@ -336,6 +344,17 @@ Status BlockPool::fork(int32_t parent, int32_t* child) {
 Status BlockPool::seq_free(int32_t seq) {
   if (!live(seq)) return kBadSeq;
   Seq& s = seqs_[seq];
+  if (s.swapped) {  // host blocks go back to the host queue; device counters were settled at swap-out
+    for (int32_t h : s.table) host_push(h);
+    std::vector<int32_t>().swap(s.table);
+    std::vector<int32_t>().swap(s.tokens);
+    s.len = 0;
+    s.swapped = false;
+    s.live = false;
+    --swapped_seqs_;
+    --live_seqs_;
+    return kOk;
+  }
   for (int32_t b : s.table) {
     if (ref_[b] == 2) --shared_;
     --ref_[b];
@@ -362,6 +381,10 @@ Status BlockPool::block_tables(const int32_t* seqs, int32_t n, int32_t max_block
     if (!live(seqs[i])) {
       *err = "pa_block_tables: unknown sequence";
       return kBadSeq;
+    }
+    if (seqs_[seqs[i]].swapped) {
+      *err = "pa_block_tables: a sequence is swapped out";
+      return kBadArg;
     }
     if (seqs_[seqs[i]].table.size() > static_cast<size_t>(max_blocks)) {
       *err = "pa_block_tables: a table is longer than max_blocks";
@@ -403,6 +426,10 @@ Status BlockPool::shared_prefix(const int32_t* seqs, int32_t n, int32_t* out,
       *err = "pa_shared_prefix: unknown sequence";
       return kBadSeq;
     }
+    if (seqs_[seqs[i]].swapped) {
+      *err = "pa_shared_prefix: a sequence is swapped out";
+      return kBadArg;
+    }
   }
   for (int32_t i = 0; i < n; ++i) {
     const Seq& s = seqs_[seqs[i]];
@@ -428,6 +455,9 @@ void BlockPool::state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) cons
     st->prompt_tokens = prompt_tokens_;
     st->hit_tokens = hit_tokens_;
     st->evictions = evictions_;
+    st->host_blocks = host_n_;
+    st->host_free_blocks = host_count_;
+    st->swapped_seqs = swapped_seqs_;
   }
   if (free_order) {
     int32_t i = 0;
@@ -436,6 +466,121 @@ void BlockPool::state(PoolStats* st, int32_t* free_order, int32_t* ref_cnt) cons
   if (ref_cnt) {
     for (int32_t b = 0; b < n_; ++b) ref_cnt[b] = ref_[b];
   }
+}
+
+int32_t BlockPool::host_pop() {
+  const int32_t h = host_free_[host_head_];
+  host_head_ = (host_head_ + 1) % host_n_;
+  --host_count_;
+  return h;
+}
+
+void BlockPool::host_push(int32_t h) {
+  host_free_[(host_head_ + host_count_) % host_n_] = h;
+  ++host_count_;
+}
+
+Status BlockPool::set_swap_space(int32_t n, std::string* err) {
+  if (n < 0) {
+    *err = "pa_swap_space: num_host_blocks < 0";
+    return kBadArg;
+  }
+  if (swapped_seqs_ > 0) {
+    *err = "pa_swap_space: sequences are swapped out";
+    return kBadArg;
+  }
+  std::vector<int32_t> q;
+  try {
+    q.resize(static_cast<size_t>(n));
+  } catch (const std::bad_alloc&) {
+    *err = "pa_swap_space: out of host memory";
+    return kCapacity;
+  }
+  for (int32_t i = 0; i < n; ++i) q[i] = i;
+  host_free_.swap(q);
+  host_n_ = n;
+  host_head_ = 0;
+  host_count_ = n;
+  return kOk;
+}
+
+Status BlockPool::swap_out(int32_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs,
+                           std::string* err) {
+  if (!live(seq)) {
+    *err = "pa_swap_out: unknown sequence";
+    return kBadSeq;
+  }
+  Seq& s = seqs_[seq];
+  const int32_t nb = static_cast<int32_t>(s.table.size());
+  if (s.swapped || n_pairs == nullptr || (nb > 0 && pairs == nullptr)) {
+    *err = s.swapped ? "pa_swap_out: the sequence is already swapped out" : "pa_swap_out: NULL argument";
+    return kBadArg;
+  }
+  if (nb > cap) {
+    *err = "pa_swap_out: pairs_out holds fewer than the sequence's blocks";
+    return kCapacity;
+  }
+  if (nb > host_count_) {
+    *err = "pa_swap_out: not enough free host blocks";
+    return kNoBlocks;
+  }
+  // --- no failure past this point ---
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t b = s.table[i];
+    const int32_t h = host_pop();
+    pairs[2 * i] = b;
+    pairs[2 * i + 1] = h;
+    if (ref_[b] == 2) --shared_;
+    --ref_[b];
+    --refs_;
+    if (ref_[b] == 0) push_back(b);
+    s.table[i] = h;
+  }
+  tokens_ -= s.len;
+  waste_ -= static_cast<int64_t>(nb) * bs_ - s.len;
+  s.swapped = true;
+  ++swapped_seqs_;
+  *n_pairs = nb;
+  return kOk;
+}
+
+Status BlockPool::swap_in(int32_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs,
+                          std::string* err) {
+  if (!live(seq)) {
+    *err = "pa_swap_in: unknown sequence";
+    return kBadSeq;
+  }
+  Seq& s = seqs_[seq];
+  const int32_t nb = static_cast<int32_t>(s.table.size());
+  if (!s.swapped || n_pairs == nullptr || (nb > 0 && pairs == nullptr)) {
+    *err = !s.swapped ? "pa_swap_in: the sequence is not swapped out" : "pa_swap_in: NULL argument";
+    return kBadArg;
+  }
+  if (nb > cap) {
+    *err = "pa_swap_in: pairs_out holds fewer than the sequence's blocks";
+    return kCapacity;
+  }
+  if (nb > nfree_) {
+    *err = "pa_swap_in: not enough free blocks";
+    return kNoBlocks;
+  }
+  // --- no failure past this point ---
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t h = s.table[i];
+    const int32_t b = pop_front();
+    ref_[b] = 1;
+    ++refs_;
+    pairs[2 * i] = h;
+    pairs[2 * i + 1] = b;
+    host_push(h);
+    s.table[i] = b;
+  }
+  tokens_ += s.len;
+  waste_ += static_cast<int64_t>(nb) * bs_ - s.len;
+  s.swapped = false;
+  --swapped_seqs_;
+  *n_pairs = nb;
+  return kOk;
 }
 
 }  // namespace pa

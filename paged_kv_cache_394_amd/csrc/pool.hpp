@@ -17,6 +17,11 @@
 // when the queue front hands them out again; a hit on a waiting block takes it
 // out of the middle of the queue.  Blocks enter the cache on cache_commit(),
 // once the caller has written their K/V.
+// Preemption by swapping ([p3] "What happens when the GPU runs out of KV
+// blocks?"): an optional pool of host (CPU RAM) blocks with its own FIFO free
+// queue; swapping a sequence out moves its table to host blocks and drops its
+// references to device blocks, swapping it in takes device blocks again.  The
+// byte copies are the caller's (pa_swap_blocks), ordered on its stream.
 // Every mutating call is all-or-nothing: it validates and reserves host memory
 // first, and only then changes state.
 #pragma once
@@ -38,7 +43,8 @@ enum Status : int32_t {
 
 struct PoolStats {
   int64_t num_blocks, free_blocks, used_blocks, shared_blocks, total_refs, cow_copies,
-      live_seqs, tokens, waste_tokens, cached_blocks, prompt_tokens, hit_tokens, evictions;
+      live_seqs, tokens, waste_tokens, cached_blocks, prompt_tokens, hit_tokens, evictions,
+      host_blocks, host_free_blocks, swapped_seqs;
 };
 
 class BlockPool {
@@ -60,6 +66,11 @@ class BlockPool {
                       int32_t* hit_tokens, std::string* err);
   // Enter the sequence's full, token-known blocks into the prefix cache.
   Status cache_commit(int32_t seq, int32_t* added, std::string* err);
+  // Host swap space of n blocks (only while no sequence is swapped out).
+  Status set_swap_space(int32_t n, std::string* err);
+  // pairs: 2 * blocks entries {device, host} (out) / {host, device} (in).
+  Status swap_out(int32_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs, std::string* err);
+  Status swap_in(int32_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs, std::string* err);
   Status fork(int32_t parent, int32_t* child);
   Status seq_free(int32_t seq);
   Status block_tables(const int32_t* seqs, int32_t n, int32_t max_blocks, int32_t* tables,
@@ -81,12 +92,15 @@ class BlockPool {
   int32_t pop_front();  // evicts the block's cache entry, if any
   void push_back(int32_t b);
   void unlink(int32_t b);  // remove from the middle of the free queue
+  int32_t host_pop();
+  void host_push(int32_t h);
   uint64_t block_hash(uint64_t parent, const int32_t* ids) const;
   // cached block for this (parent key, ids), or -1
   int32_t lookup(uint64_t key, uint64_t parent, const int32_t* ids) const;
 
   struct Seq {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;  // device blocks, or host blocks while swapped
+    bool swapped = false;
     std::vector<int32_t> tokens;  // ids of the leading tokens, while every append gave them
     int64_t len = 0;
     bool live = false;
@@ -107,6 +121,11 @@ class BlockPool {
   std::unordered_map<uint64_t, int32_t> cache_;   // key -> block
   std::unordered_map<int32_t, Cached> cached_;    // block -> its entry
   int64_t prompt_tokens_ = 0, hit_tokens_ = 0, evictions_ = 0;
+  // host swap space: FIFO free queue of host block ids
+  int32_t host_n_ = 0;
+  std::vector<int32_t> host_free_;  // ring buffer of host_n_ entries
+  int32_t host_head_ = 0, host_count_ = 0;
+  int64_t swapped_seqs_ = 0;
 };
 
 }  // namespace pa

@@ -22,7 +22,7 @@ def assert_same_state(lib_pool, orc: OraclePool):
         t, ln = pa.pa_seq_table(lib_pool, sid)
         assert t.tolist() == orc.table(sid) and ln == orc.lens[sid]
     # shared prefix: leading table entries whose block more than one table holds
-    sids = sorted(orc.tables)
+    sids = sorted(x for x in orc.tables if x not in orc.swapped)
     got = pa.pa_shared_prefix(lib_pool, sids).tolist()
     want = []
     for sid in sids:
@@ -92,6 +92,18 @@ class Pair:
         assert lib_st == st_
         if st_ == Status.OK:
             assert added == oadded
+
+    def swap(self, s, out: bool):
+        try:
+            pairs = (pa.pa_swap_out if out else pa.pa_swap_in)(self.lib, s)
+            lib_st = Status.OK
+        except pa.PaError as e:
+            lib_st, pairs = e.name, None
+        st_, opairs = (self.orc.swap_out if out else self.orc.swap_in)(s)
+        assert lib_st == st_
+        if st_ == Status.OK:
+            assert [tuple(x) for x in pairs.tolist()] == opairs
+        return st_
 
     def fork(self, s):
         try:
@@ -297,3 +309,52 @@ def test_prefix_cache_errors_and_hit_rate():
     assert pa.lib.pa_alloc_prompt(p.lib.handle, c, None, 5, None, None) == pa.PA_ERR_BAD_ARG
     assert pa.lib.pa_append_tokens(p.lib.handle, c, None, 5, None, None) == pa.PA_ERR_BAD_ARG
     assert pa.lib.pa_cache_commit(p.lib.handle, 999, None) == pa.PA_ERR_BAD_SEQ
+
+
+swap_ops = st.lists(st.tuples(st.sampled_from(["new", "prompt", "append_tokens", "append", "commit",
+                                               "fork", "free", "out", "in", "space"]),
+                              st.integers(0, 50), st.integers(0, 70), st.integers(0, 3)),
+                    min_size=1, max_size=60)
+
+
+@settings(max_examples=200, deadline=None)
+@given(ops=swap_ops, n=st.integers(2, 24), host=st.integers(0, 30), bs=st.sampled_from([1, 3, 16]),
+       seed=st.integers(0, 999))
+def test_swap_ops_match_oracle(ops, n, host, bs, seed):
+    """Swapping out and in, mixed with prefix caching, forks and frees: every
+    pair list, table, count and queue order equals the oracle's."""
+    r = random.Random(seed)
+    p = Pair(n, bs)
+    pa.pa_swap_space(p.lib, host)
+    assert p.orc.set_swap_space(host) == Status.OK
+    bases = [[r.randrange(3) for _ in range(80)] for _ in range(3)]
+    live = []
+    for op, i, k, which in ops:
+        if op == "new" or not live:
+            live.append(p.create())
+        elif op == "prompt":
+            s = p.create()
+            p.prompt(s, bases[which % 3][:k] + [r.randrange(3) for _ in range(i % 7)])
+            live.append(s)
+        elif op == "append_tokens":
+            p.append_tokens(live[i % len(live)], [r.randrange(3) for _ in range(k % 20)])
+        elif op == "append":
+            p.append(live[i % len(live)], k % 20)
+        elif op == "commit":
+            p.commit(live[i % len(live)])
+        elif op == "fork":
+            c = p.fork(live[i % len(live)])
+            if c >= 0:
+                live.append(c)
+        elif op == "free":
+            p.free(live.pop(i % len(live)))
+        elif op == "space":
+            try:
+                pa.pa_swap_space(p.lib, k % 30)
+                lib_st = Status.OK
+            except pa.PaError as e:
+                lib_st = e.name
+            assert lib_st == p.orc.set_swap_space(k % 30)
+        else:
+            p.swap(live[i % len(live)], op == "out")
+        p.check()

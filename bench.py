@@ -16,6 +16,8 @@ Reported on one JSON line:
                logical K/V bytes
   prefix_cache multi-turn dialogues through the prefix cache: hit rate and
                block-manager call times (host only)
+  mixed_step   the prefill and decode batches over one cache in one launch
+               (pa_mixed_step) against two launches
   preemption   one 2048-token sequence swapped to pinned host memory and back
                (PCIe GB/s), against its attention-side recomputation
   prefill      chunked prefill, 8 x 512-token chunks over 0..4096 cached tokens,
@@ -63,7 +65,7 @@ def log(msg):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "device_common.hpp"):
+    for name in ("decode.hip", "decode_impl.hpp", "device_common.hpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_394_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -357,6 +359,56 @@ def bench_preemption(pa, torch, np, workloads, reps=10):
             "recompute_attention_ms_per_layer": round(mean, 3)}
 
 
+def bench_mixed(pa, torch, np, workloads, reps):
+    """A continuous-batching step: the chunked-prefill batch (8 x 512 rows) and
+    the 13B-shaped decode batch (64 sequences) over one cache, as one
+    pa_mixed_step launch against pa_prefill_chunk followed by pa_decode."""
+    wp, wd = workloads.chunked_prefill(), workloads.llama13b_decode()
+    n = wp.num_blocks + wd.num_blocks
+    pool = pa.pa_pool_create(n, 16)
+    cache = pa.KvCache(n, wd.num_kv_heads, wd.head_dim)
+    pids, dids = [], []
+    for b in range(wp.batch):
+        s = pa.pa_seq_create(pool)
+        pids.append(s)
+        k, v = wp.kv(b)
+        slots, _ = pa.pa_alloc_append(pool, s, int(wp.lens[b]))
+        pa.pa_write_kv(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda())
+    for b in range(wd.batch):
+        s = pa.pa_seq_create(pool)
+        dids.append(s)
+        k, v = wd.kv(b)
+        slots, _ = pa.pa_alloc_append(pool, s, int(wd.lens[b]))
+        pa.pa_write_kv(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda())
+    tp, _ = pa.pa_block_tables(pool, pids, -(-int(wp.lens.max()) // 16))
+    max_ctx = int(wd.lens.max())
+    td, lens = pa.pa_block_tables(pool, dids, -(-max_ctx // 16))
+    cu = np.concatenate([[0], np.cumsum(wp.chunk)]).astype(np.int32)
+    prefill = dict(q=torch.from_numpy(wp.q).cuda(), cu_q=torch.from_numpy(cu).cuda(),
+                   prior=torch.from_numpy(wp.prior.astype(np.int32)).cuda(), tables=torch.from_numpy(tp).cuda(),
+                   max_chunk=int(wp.chunk.max()),
+                   out=torch.empty((int(cu[-1]), wp.num_heads, wp.head_dim), dtype=torch.float32, device="cuda"))
+    decode = dict(q=torch.from_numpy(wd.q).cuda(), tables=torch.from_numpy(td).cuda(),
+                  lens=torch.from_numpy(lens).cuda(), max_context_len=max_ctx,
+                  out=torch.empty((wd.batch, wd.num_heads, wd.head_dim), dtype=torch.float32, device="cuda"),
+                  workspace=torch.empty(max(16, pa.pa_decode_workspace_bytes(wd.batch, wd.num_heads, wd.head_dim,
+                                                                             max_ctx)), dtype=torch.uint8,
+                                        device="cuda"))
+    scale = wp.scale
+
+    def separate():
+        pa.pa_prefill_chunk(cache, prefill["q"], prefill["cu_q"], prefill["prior"], prefill["tables"],
+                            prefill["max_chunk"], scale, prefill["out"])
+        pa.pa_decode(cache, decode["q"], decode["tables"], decode["lens"], max_ctx, scale, decode["out"],
+                     decode["workspace"])
+
+    mixed_ms, _ = time_events(torch, lambda: pa.pa_mixed_step(cache, scale, prefill, decode), reps)
+    sep_ms, _ = time_events(torch, separate, reps)
+    return {"workload": "chunked_prefill (8 x 512 rows) + llama13b_decode (64 seqs) over one cache",
+            "mixed_ms": round(mixed_ms, 4), "separate_ms": round(sep_ms, 4),
+            "speedup": round(sep_ms / mixed_ms, 3)}
+
+
 def bench_prefill(pa, torch, np, workloads, reps):
     w = workloads.chunked_prefill()
     pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
@@ -600,6 +652,9 @@ def main():
         torch.cuda.empty_cache()
         log("prefix cache (host)")
         res["prefix_cache"] = bench_prefix_cache(pa, np, workloads)
+        log("mixed prefill + decode step")
+        res["mixed_step"] = bench_mixed(pa, torch, np, workloads, 20)
+        torch.cuda.empty_cache()
         log("preemption: swap vs recompute")
         res["preemption"] = bench_preemption(pa, torch, np, workloads)
         torch.cuda.empty_cache()

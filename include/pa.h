@@ -253,6 +253,44 @@ pa_status pa_write_kv(const pa_kv_cache *cache, const void *k_new, const void *v
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len);
 
+/* One continuous-batching step in one launch ([p1] "Chunked Prefill" and
+ * "Mechanics of Chunked Prefill": prefill chunks of admitted requests are
+ * scheduled in the same step as the decode of running ones; [p3] continuous
+ * batching section).  Computes exactly what pa_prefill_chunk(prefill) and
+ * pa_decode(decode) compute, over one cache (one layer), in one kernel whose
+ * grid holds the prefill workgroups first and the decode workgroups after
+ * them, so decode work fills the CUs the prefill's tail leaves idle.
+ * prefill / decode: either may be NULL or empty (batch 0); fields as the
+ * arguments of the two calls.  fp16 caches (an e4m3 cache allows decode only).
+ * The one-launch form covers decode contexts up to 16384 tokens; beyond that,
+ * or with one part empty, the parts are launched one after the other on the
+ * same stream (same results), which is when decode->workspace may be needed
+ * (size as pa_decode_workspace_bytes).  Errors: as the two calls. */
+typedef struct {
+  const void *q;           /* device fp16 [total_q][num_heads][head_dim]            */
+  int32_t total_q;
+  const int32_t *cu_q;     /* device int32[batch + 1]                               */
+  const int32_t *prior;    /* device int32[batch]                                   */
+  const int32_t *tables;   /* device int32[batch][max_blocks]                       */
+  int32_t batch, max_blocks, max_chunk;
+  float *out;              /* device fp32 [total_q][num_heads][head_dim]            */
+} pa_prefill_batch;
+
+typedef struct {
+  const void *q;           /* device fp16 [batch][num_heads][head_dim]              */
+  const int32_t *tables;   /* device int32[batch][max_blocks]                       */
+  const int32_t *lens;     /* device int32[batch]                                   */
+  const int32_t *cached_blocks; /* NULL or device int32[batch] (pa_decode's hint)   */
+  int32_t batch, max_blocks, max_context_len;
+  float *out;              /* device fp32 [batch][num_heads][head_dim]              */
+  void *workspace;         /* device, only for the two-launch fallback              */
+  size_t workspace_bytes;
+} pa_decode_batch;
+
+pa_status pa_mixed_step(const pa_kv_cache *cache, int32_t num_heads, float scale,
+                        const pa_prefill_batch *prefill, const pa_decode_batch *decode,
+                        void *hip_stream);
+
 /* Copy whole blocks between the device cache and caller-owned host memory, for
  * pa_swap_out / pa_swap_in.  host_k / host_v: host buffers of num_host_blocks
  * blocks each, in the cache's layout [block][num_kv_heads][block_size][head_dim]

@@ -66,6 +66,20 @@ class pa_pool_stats(ctypes.Structure):
         "evictions", "host_blocks", "host_free_blocks", "swapped_seqs")]
 
 
+class pa_prefill_batch(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("total_q", ctypes.c_int32), ("cu_q", ctypes.c_void_p),
+                ("prior", ctypes.c_void_p), ("tables", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("max_chunk", ctypes.c_int32), ("out", ctypes.c_void_p)]
+
+
+class pa_decode_batch(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("tables", ctypes.c_void_p), ("lens", ctypes.c_void_p),
+                ("cached_blocks", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 # every symbol include/pa.h declares, with its ctypes signature
 _SIGNATURES = {
     "pa_pool_create": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.POINTER(ctypes.c_void_p)]),
@@ -99,6 +113,9 @@ _SIGNATURES = {
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                           ctypes.c_void_p, ctypes.c_void_p]),
+    "pa_mixed_step": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_int32, ctypes.c_float,
+                                       ctypes.POINTER(pa_prefill_batch), ctypes.POINTER(pa_decode_batch),
+                                       ctypes.c_void_p]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_char_p, []),
 }
@@ -368,6 +385,41 @@ def pa_swap_blocks(cache: "KvCache", host_k: torch.Tensor, host_v: torch.Tensor,
     _check(lib.pa_swap_blocks(ctypes.byref(cache.desc), host_k.data_ptr(), host_v.data_ptr(),
                               int(host_k.shape[0]), _p(pr) if len(pr) else None, len(pr), direction,
                               _stream(stream)))
+
+
+def pa_mixed_step(cache: "KvCache", scale: float, prefill: Optional[dict] = None,
+                  decode: Optional[dict] = None, stream=None) -> None:
+    """One launch for a prefill batch and a decode batch over one cache.
+
+    prefill: dict(q [sum C][Hq][D] fp16, cu_q int32[B+1], prior int32[B],
+    tables int32[B][max_blocks], max_chunk, out fp32) -- as pa_prefill_chunk.
+    decode: dict(q [B][Hq][D] fp16, tables, lens, max_context_len, out fp32,
+    optional workspace, cached_blocks) -- as pa_decode."""
+    pb = db = None
+    hq = None
+    if prefill is not None:
+        q = prefill["q"]
+        total, hq, _ = q.shape
+        B = int(prefill["prior"].numel())
+        pb = pa_prefill_batch(_dev(q, torch.float16), total, _dev(prefill["cu_q"], torch.int32),
+                              _dev(prefill["prior"], torch.int32), _dev(prefill["tables"], torch.int32),
+                              B, prefill["tables"].shape[1], int(prefill["max_chunk"]),
+                              _dev(prefill["out"], torch.float32))
+    if decode is not None:
+        q = decode["q"]
+        B, hq_d, _ = q.shape
+        hq = hq_d if hq is None else hq
+        ws = decode.get("workspace")
+        cb = decode.get("cached_blocks")
+        db = pa_decode_batch(_dev(q, torch.float16), _dev(decode["tables"], torch.int32),
+                             _dev(decode["lens"], torch.int32),
+                             None if cb is None else _dev(cb, torch.int32), B, decode["tables"].shape[1],
+                             int(decode["max_context_len"]), _dev(decode["out"], torch.float32),
+                             None if ws is None else ws.data_ptr(),
+                             0 if ws is None else ws.numel() * ws.element_size())
+    _check(lib.pa_mixed_step(ctypes.byref(cache.desc), hq or 1, scale,
+                             None if pb is None else ctypes.byref(pb),
+                             None if db is None else ctypes.byref(db), _stream(stream)))
 
 
 def version() -> str:

@@ -47,9 +47,57 @@ pa_status hip_status(hipError_t e, const char* fn) {
   return pa::ok();
 }
 
+// Argument checks shared by pa_decode and pa_mixed_step (PA_OK when valid).
+pa_status check_decode(const pa::KvDesc& d, const std::string& fn, int32_t num_heads, const void* q,
+                       const int32_t* tables_dev, const int32_t* lens_dev, int32_t B,
+                       int32_t max_blocks, int32_t max_context_len, float scale,
+                       const float* out_dev, const void* workspace_dev, size_t workspace_bytes) {
+  if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
+    return fail(PA_ERR_BAD_ARG, fn + ": num_heads must be a positive multiple of num_kv_heads");
+  if (B < 0 || max_blocks < 1 || max_context_len < 0)
+    return fail(PA_ERR_BAD_ARG, fn + ": bad B / max_blocks / max_context_len");
+  if (B == 0) return PA_OK;
+  if (q == nullptr || tables_dev == nullptr || lens_dev == nullptr || out_dev == nullptr)
+    return fail(PA_ERR_BAD_ARG, fn + ": NULL device pointer");
+  if (!aligned16(q) || !aligned16(out_dev)) return fail(PA_ERR_BAD_ARG, fn + ": q / out must be 16-byte aligned");
+  if (num_heads > 65535 || B > 65535) return fail(PA_ERR_BAD_ARG, fn + ": num_heads and B must be <= 65535");
+  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, fn + ": scale must be finite");
+  if (pa::decode_units(B, num_heads, max_context_len) > (int64_t(1) << 31) - 64)
+    return fail(PA_ERR_BAD_ARG, fn + ": B * num_heads * ceil(max_context_len / 256) too large for one launch");
+  const size_t need = pa::decode_workspace_bytes(B, num_heads, d.head_dim, max_context_len);
+  if (workspace_bytes < need || (need > 0 && workspace_dev == nullptr))
+    return fail(PA_ERR_BAD_ARG, fn + ": workspace smaller than pa_decode_workspace_bytes()");
+  if (need > 0 && !aligned16(workspace_dev))
+    return fail(PA_ERR_BAD_ARG, fn + ": workspace must be 16-byte aligned");
+  return PA_OK;
+}
+
+// Argument checks shared by pa_prefill_chunk and pa_mixed_step.
+pa_status check_prefill(const pa::KvDesc& d, const std::string& fn, int32_t num_heads, const void* q,
+                        int32_t total_q_rows, const int32_t* cu_q_dev, const int32_t* prior_dev,
+                        const int32_t* tables_dev, int32_t B, int32_t max_blocks, int32_t max_chunk,
+                        float scale, const float* out_dev) {
+  if (d.fp8) return fail(PA_ERR_UNSUPPORTED, fn + ": e4m3 caches are decode-only");
+  if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
+    return fail(PA_ERR_BAD_ARG, fn + ": num_heads must be a positive multiple of num_kv_heads");
+  if (B < 0 || max_blocks < 1 || max_chunk < 0 || total_q_rows < 0)
+    return fail(PA_ERR_BAD_ARG, fn + ": bad B / max_blocks / max_chunk / total_q_rows");
+  if (B == 0 || total_q_rows == 0 || max_chunk == 0) return PA_OK;
+  if (q == nullptr || cu_q_dev == nullptr || prior_dev == nullptr || tables_dev == nullptr ||
+      out_dev == nullptr)
+    return fail(PA_ERR_BAD_ARG, fn + ": NULL device pointer");
+  if (!aligned16(q) || !aligned16(out_dev))
+    return fail(PA_ERR_BAD_ARG, fn + ": q / out must be 16-byte aligned");
+  if (num_heads > 65535 || B > 65535)
+    return fail(PA_ERR_BAD_ARG, fn + ": num_heads and B must be <= 65535");
+  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, fn + ": scale must be finite");
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
 
 pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new,
                       const int32_t* slots_dev, int32_t T, const int32_t* cow_pairs_host,
@@ -93,23 +141,11 @@ pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
   const char* fn = "pa_decode";
   pa::KvDesc d;
   if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
-  if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
-    return fail(PA_ERR_BAD_ARG, "pa_decode: num_heads must be a positive multiple of num_kv_heads");
-  if (B < 0 || max_blocks < 1 || max_context_len < 0)
-    return fail(PA_ERR_BAD_ARG, "pa_decode: bad B / max_blocks / max_context_len");
+  if (pa_status st = check_decode(d, fn, num_heads, q, tables_dev, lens_dev, B, max_blocks,
+                                  max_context_len, scale, out_dev, workspace_dev, workspace_bytes);
+      st != PA_OK)
+    return st;
   if (B == 0) return pa::ok();
-  if (q == nullptr || tables_dev == nullptr || lens_dev == nullptr || out_dev == nullptr)
-    return fail(PA_ERR_BAD_ARG, "pa_decode: NULL device pointer");
-  if (!aligned16(q) || !aligned16(out_dev)) return fail(PA_ERR_BAD_ARG, "pa_decode: q / out must be 16-byte aligned");
-  if (num_heads > 65535 || B > 65535) return fail(PA_ERR_BAD_ARG, "pa_decode: num_heads and B must be <= 65535");
-  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, "pa_decode: scale must be finite");
-  if (pa::decode_units(B, num_heads, max_context_len) > (int64_t(1) << 31) - 64)
-    return fail(PA_ERR_BAD_ARG, "pa_decode: B * num_heads * ceil(max_context_len / 256) too large for one launch");
-  const size_t need = pa::decode_workspace_bytes(B, num_heads, d.head_dim, max_context_len);
-  if (workspace_bytes < need || (need > 0 && workspace_dev == nullptr))
-    return fail(PA_ERR_BAD_ARG, "pa_decode: workspace smaller than pa_decode_workspace_bytes()");
-  if (need > 0 && !aligned16(workspace_dev))
-    return fail(PA_ERR_BAD_ARG, "pa_decode: workspace must be 16-byte aligned");
   return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, cached_blocks_dev, B,
                                       max_blocks, max_context_len, scale, out_dev, workspace_dev,
                                       static_cast<hipStream_t>(hip_stream)),
@@ -123,24 +159,64 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t num_
   const char* fn = "pa_prefill_chunk";
   pa::KvDesc d;
   if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
-  if (d.fp8) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: e4m3 caches are decode-only");
-  if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
-    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: num_heads must be a positive multiple of num_kv_heads");
-  if (B < 0 || max_blocks < 1 || max_chunk < 0 || total_q_rows < 0)
-    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: bad B / max_blocks / max_chunk / total_q_rows");
+  if (pa_status st = check_prefill(d, fn, num_heads, q, total_q_rows, cu_q_dev, prior_dev, tables_dev,
+                                   B, max_blocks, max_chunk, scale, out_dev);
+      st != PA_OK)
+    return st;
   if (B == 0 || total_q_rows == 0 || max_chunk == 0) return pa::ok();
-  if (q == nullptr || cu_q_dev == nullptr || prior_dev == nullptr || tables_dev == nullptr ||
-      out_dev == nullptr)
-    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: NULL device pointer");
-  if (!aligned16(q) || !aligned16(out_dev))
-    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: q / out must be 16-byte aligned");
-  if (num_heads > 65535 || B > 65535)
-    return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: num_heads and B must be <= 65535");
-  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, "pa_prefill_chunk: scale must be finite");
   return hip_status(pa::launch_prefill(d, q, num_heads, total_q_rows, cu_q_dev, prior_dev,
                                        tables_dev, B, max_blocks, max_chunk, scale, out_dev,
                                        static_cast<hipStream_t>(hip_stream)),
                     fn);
+}
+
+pa_status pa_mixed_step(const pa_kv_cache* cache, int32_t num_heads, float scale,
+                        const pa_prefill_batch* prefill, const pa_decode_batch* decode,
+                        void* hip_stream) {
+  const char* fn = "pa_mixed_step";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  const bool has_p = prefill != nullptr && prefill->batch > 0 && prefill->total_q > 0 &&
+                     prefill->max_chunk > 0;
+  const bool has_d = decode != nullptr && decode->batch > 0;
+  if (prefill != nullptr) {
+    const pa_prefill_batch& p = *prefill;
+    if (pa_status st = check_prefill(d, fn, num_heads, p.q, p.total_q, p.cu_q, p.prior, p.tables,
+                                     p.batch, p.max_blocks, p.max_chunk, scale, p.out);
+        st != PA_OK)
+      return st;
+  }
+  if (decode != nullptr) {
+    const pa_decode_batch& q = *decode;
+    if (pa_status st = check_decode(d, fn, num_heads, q.q, q.tables, q.lens, q.batch, q.max_blocks,
+                                    q.max_context_len, scale, q.out, q.workspace, q.workspace_bytes);
+        st != PA_OK)
+      return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (has_p && has_d && decode->max_context_len <= pa::mixed_max_context()) {
+    const pa::MixedPrefill mp{prefill->q, prefill->total_q, prefill->cu_q, prefill->prior,
+                              prefill->tables, prefill->batch, prefill->max_blocks,
+                              prefill->max_chunk, prefill->out};
+    const pa::MixedDecode md{decode->q, decode->tables, decode->lens, decode->cached_blocks,
+                             decode->batch, decode->max_blocks, decode->max_context_len, decode->out};
+    return hip_status(pa::launch_mixed(d, num_heads, scale, mp, md, s), fn);
+  }
+  // one part only, or decode contexts beyond the mixed launch: separate launches
+  if (has_p) {
+    const hipError_t e = pa::launch_prefill(d, prefill->q, num_heads, prefill->total_q, prefill->cu_q,
+                                            prefill->prior, prefill->tables, prefill->batch,
+                                            prefill->max_blocks, prefill->max_chunk, scale,
+                                            prefill->out, s);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  if (has_d)
+    return hip_status(pa::launch_decode(d, decode->q, num_heads, decode->tables, decode->lens,
+                                        decode->cached_blocks, decode->batch, decode->max_blocks,
+                                        decode->max_context_len, scale, decode->out,
+                                        decode->workspace, s),
+                      fn);
+  return pa::ok();
 }
 
 pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v,

@@ -41,4 +41,24 @@ hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t to
                           int32_t B, int32_t max_blocks, int32_t max_chunk, float scale, float* out,
                           hipStream_t s);
 
+// Mixed step: chunked prefill of some sequences and decode of others in one
+// launch (fp16 caches).  The decode half supports contexts up to
+// mixed_max_context() tokens; the caller falls back to two launches beyond.
+struct MixedPrefill {
+  const void* q;
+  int32_t total_q;
+  const int32_t *cu_q, *prior, *tables;
+  int32_t B, max_blocks, max_chunk;
+  float* out;
+};
+struct MixedDecode {
+  const void* q;
+  const int32_t *tables, *lens, *cached;
+  int32_t B, max_blocks, max_ctx;
+  float* out;
+};
+int32_t mixed_max_context();
+hipError_t launch_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
+                        const MixedDecode& d, hipStream_t s);
+
 }  // namespace pa

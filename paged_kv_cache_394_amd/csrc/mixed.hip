@@ -1,0 +1,87 @@
+// One launch for a whole continuous-batching step: the chunked-prefill
+// workgroups of the sequences being admitted and the decode workgroups of the
+// running ones ([p1] "Chunked Prefill": prefill chunks are scheduled together
+// with decode requests in the same step; [p3] continuous batching section: the
+// batch is refilled at every iteration).
+//
+// The grid holds every prefill workgroup first, then one decode workgroup per
+// (sequence, head).  The dispatcher hands out workgroups in id order, so the
+// decode workgroups start as soon as prefill workgroups retire: the
+// HBM-bound decode fills the CUs that the MFMA-bound prefill leaves idle in its
+// tail, instead of running after it.  Both halves are the standalone kernels'
+// bodies (prefill_body, decode_seq_body with 4 waves), bit-identical in result;
+// the decode half runs at the prefill's occupancy (2 workgroups per CU).
+#include "decode_impl.hpp"
+#include "prefill_impl.hpp"
+
+namespace pa {
+namespace {
+
+using namespace dev;
+
+// per-sequence decode inside the mixed launch: 2 blocks per step, not
+// pipelined, 4 waves (the standalone fp16 per-sequence configuration)
+constexpr int kMixU = 2;
+constexpr int kMixW = 4;
+static_assert(kMixW * 64 == kThreads, "decode and prefill workgroups have one shape");
+
+template <int D, int kTR>
+__global__ __launch_bounds__(kThreads, 2) void mixed_step_kernel(
+    const half_t* __restrict__ pq, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
+    const int32_t* __restrict__ ptables, float* __restrict__ pout, int32_t Bp, int32_t Hq,
+    int32_t Hkv, int32_t total_q, int32_t pmax_blocks, int32_t num_blocks, int32_t nqt,
+    float qk_scale, int32_t n_prefill_wgs, const half_t* __restrict__ dq,
+    const int32_t* __restrict__ dtables, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ cached, float* __restrict__ dout, int32_t Bd, int32_t dmax_blocks,
+    int32_t ctx_cap) {
+  const int wg = blockIdx.x;
+  if (wg < n_prefill_wgs) {
+    prefill_body<D>(wg, pq, kc, vc, cu_q, prior, ptables, pout, Bp, Hq, Hkv, total_q, pmax_blocks,
+                    num_blocks, nqt, qk_scale);
+  } else {
+    decode_seq_body<D, false, kMixU, false, kMixW, kTR>(
+        wg - n_prefill_wgs, dq, reinterpret_cast<const uint8_t*>(kc),
+        reinterpret_cast<const uint8_t*>(vc), dtables, lens, cached, dout, Bd, Hq, Hkv, dmax_blocks,
+        ctx_cap, num_blocks, qk_scale, 1.0f);
+  }
+}
+
+template <int D, int kTR>
+hipError_t run_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
+                     const MixedDecode& d, hipStream_t s) {
+  const int32_t nqt = (p.max_chunk + kBq - 1) / kBq;
+  const int64_t pairs = static_cast<int64_t>(p.B) * Hq;
+  const int64_t n_prefill = (pairs + kXcds - 1) / kXcds * kXcds * nqt;
+  const int64_t n_decode = static_cast<int64_t>(d.B) * Hq;
+  const int32_t ctx_cap =
+      static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * kBlock, d.max_ctx));
+  mixed_step_kernel<D, kTR><<<dim3(static_cast<uint32_t>(n_prefill + n_decode)), dim3(kThreads), 0, s>>>(
+      static_cast<const half_t*>(p.q), static_cast<const half_t*>(c.k),
+      static_cast<const half_t*>(c.v), p.cu_q, p.prior, p.tables, p.out, p.B, Hq, c.num_kv_heads,
+      p.total_q, p.max_blocks, c.num_blocks, nqt, scale * kLog2e, static_cast<int32_t>(n_prefill),
+      static_cast<const half_t*>(d.q), d.tables, d.lens, d.cached, d.out, d.B, d.max_blocks, ctx_cap);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int32_t mixed_max_context() { return 64 * 4 * kMixW * kBlock; }
+
+hipError_t launch_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
+                        const MixedDecode& d, hipStream_t s) {
+  // blocks per decode wave decide the block-id registers (64 per register)
+  const int64_t ctx = std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * kBlock, d.max_ctx);
+  const int64_t per_wave = ((ctx + kBlock - 1) / kBlock + kMixW - 1) / kMixW;
+  const int tr = per_wave <= 64 ? 1 : per_wave <= 128 ? 2 : 4;
+  if (c.head_dim == 128) {
+    if (tr == 1) return run_mixed<128, 1>(c, Hq, scale, p, d, s);
+    if (tr == 2) return run_mixed<128, 2>(c, Hq, scale, p, d, s);
+    return run_mixed<128, 4>(c, Hq, scale, p, d, s);
+  }
+  if (tr == 1) return run_mixed<64, 1>(c, Hq, scale, p, d, s);
+  if (tr == 2) return run_mixed<64, 2>(c, Hq, scale, p, d, s);
+  return run_mixed<64, 4>(c, Hq, scale, p, d, s);
+}
+
+}  // namespace pa

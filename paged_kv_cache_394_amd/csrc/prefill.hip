@@ -43,423 +43,11 @@
 // (sequence, head) are given workgroup ids 8 apart, which the dispatcher sends
 // to the same XCD: they read the same K/V tiles at about the same time and
 // share that XCD's L2.
-#include <cmath>
-
-#include "device_common.hpp"
-#include "launch.hpp"
+#include "prefill_impl.hpp"
 
 namespace pa {
 namespace {
-
 using namespace dev;
-
-constexpr int kBq = 128;       // query rows per workgroup
-constexpr int kBk = 64;        // keys per tile
-constexpr int kThreads = 256;
-constexpr int kXcds = 8;       // workgroup ids are dealt round robin over 8 XCDs
-constexpr float kLazyRescale = 8.0f;  // log2 growth of a row max that forces a rescale
-
-template <int D>
-struct PGeom {
-  // K is stored row-major without padding; the 16-byte chunk c of key row r
-  // sits at chunk c ^ kswz(r).  V^T rows (one per head-dim column) hold the
-  // tile's 64 keys as 8 granules of 8 keys: granule 4 p + g of a row holds
-  // keys 32 p + 16 hb + 4 g + i (hb < 2, i < 4) at slot 4 hb + i, which is
-  // exactly the 8 keys lane group g feeds to one P.V MFMA; granule q of row r
-  // sits at q ^ vswz(r).  Both swizzles keep the MFMA operand reads and the
-  // staging stores free of bank conflicts.
-  static constexpr int DK = D / 32;         // MFMA steps over head_dim for S
-  static constexpr int DT = D / 16;         // 16-wide output tiles over head_dim
-  static constexpr int CPR = D / 8;         // 16-byte chunks per K row
-  static constexpr int KLOADS = kBk * CPR / kThreads;  // K chunks per thread
-  static constexpr int VTHREADS = 8 * (D / 4);         // threads staging V: granule x column quad
-  static constexpr int KBUF = kBk * D;      // halfs per K buffer
-  static constexpr int VBUF = D * kBk;      // halfs per V^T buffer
-  static_assert(kBk * CPR % kThreads == 0, "K tile must split evenly");
-  static_assert(16 * CPR % 64 == 0, "a wave's K chunks must stay in one block");
-  static_assert(VTHREADS <= kThreads && VTHREADS % 64 == 0, "V staging must fill whole waves");
-};
-
-__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 2)) & 7; }
-
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  if constexpr (D == 128) return r & 15;
-  else return swz8(r);
-}
-
-// Registers holding one K/V tile between its global loads and its LDS stores.
-template <int D>
-struct Stage {
-  u32x4_t k[PGeom<D>::KLOADS];
-  u32x2_t v[8];   // keys 4 g + i of block 2 p (v[i]) and of block 2 p + 1 (v[4 + i])
-};
-
-// Rank of lane b's sequence (b < B <= 64) by total length, longest first,
-// ties by index; lanes >= B get rank 64.
-__device__ __forceinline__ int work_rank(int Wb, int lane, int B) {
-  int rank = 0;
-  for (int k = 0; k < B; ++k) {
-    const int Wk = __builtin_amdgcn_readlane(Wb, k);
-    rank += (Wk > Wb || (Wk == Wb && k < lane)) ? 1 : 0;
-  }
-  return lane < B ? rank : 64;
-}
-
-// The 4 block ids of a key tile (wave-uniform scalar loads; ids past the
-// table's end, or outside the pool, read as block 0), as four scalars.
-struct TileBlocks {
-  int p0, p1, p2, p3;
-};
-
-// Block j (0..3) of a tile.  A free function on values: as a member reading
-// this->pN the selects are folded into one indexed load and the struct is
-// left in memory.
-__device__ __forceinline__ int pick_block(int j, int p0, int p1, int p2, int p3) {
-  const int lo = (j & 1) ? p1 : p0;
-  const int hi = (j & 1) ? p3 : p2;
-  return (j & 2) ? hi : lo;
-}
-
-__device__ __forceinline__ int table_id(const int32_t* __restrict__ trow, int idx, int max_blocks,
-                                        int num_blocks) {
-  int v = idx < max_blocks ? trow[idx] : 0;
-  v = __builtin_amdgcn_readfirstlane(v);
-  return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
-}
-
-// Lanes 0..3 load the 4 table entries of tile kt (a vector load, waited on
-// in order with the tile loads, one tile ahead of use).
-__device__ __forceinline__ int tile_ids_lanes(const int32_t* __restrict__ trow, int kt, int max_blocks,
-                                              int lane) {
-  const int j = kt * (kBk / kBlock) + lane;
-  return (lane < 4 && j < max_blocks) ? trow[j] : 0;
-}
-
-__device__ __forceinline__ int clamp_id(int v, int num_blocks) {
-  return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
-}
-
-__device__ __forceinline__ TileBlocks tile_blocks_from(int ids, int num_blocks) {
-  return TileBlocks{clamp_id(__builtin_amdgcn_readlane(ids, 0), num_blocks),
-                    clamp_id(__builtin_amdgcn_readlane(ids, 1), num_blocks),
-                    clamp_id(__builtin_amdgcn_readlane(ids, 2), num_blocks),
-                    clamp_id(__builtin_amdgcn_readlane(ids, 3), num_blocks)};
-}
-
-__device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ trow, int kt,
-                                                  int max_blocks, int num_blocks) {
-  const int j0 = kt * (kBk / kBlock);
-  return TileBlocks{table_id(trow, j0, max_blocks, num_blocks),
-                    table_id(trow, j0 + 1, max_blocks, num_blocks),
-                    table_id(trow, j0 + 2, max_blocks, num_blocks),
-                    table_id(trow, j0 + 3, max_blocks, num_blocks)};
-}
-
-// Per-thread staging geometry.  K load i of thread t is 16-byte chunk
-// i * 256 + t of the tile: key (i * 256 + t) / CPR, which lies in block
-// (i * 256 + 64 w) / (16 CPR) of the tile for wave w (the same for the whole
-// wave) at the same in-block row and column for every i.  Thread t < VTHREADS
-// stages V granule q = t / (D/4) (pair p = q / 4, group g = q % 4) for
-// columns 4 dq .. 4 dq + 3, dq = t % (D/4): rows 4 g .. 4 g + 3 of blocks
-// 2 p and 2 p + 1 of the tile (one pair of blocks per wave).
-template <int D>
-struct StageGeom {
-  int k_off;    // halfs from a block's (kv head) base to the thread's K chunk
-  int k_row;    // the chunk's key within the tile, for i = 0 (adds 256 i / CPR)
-  int k_col;    // its chunk index
-  bool v_on;    // thread stages V
-  int vq, dq;   // granule (0..7) and column quad
-  int v_off;    // halfs from a block's (kv head) base to row 4 g, column 4 dq
-
-  __device__ void init(int tid, int kvh) {
-    using G = PGeom<D>;
-    k_row = tid / G::CPR;
-    k_col = tid % G::CPR;
-    k_off = (kvh * kBlock + (k_row & 15)) * D + k_col * 8;
-    v_on = tid < G::VTHREADS;
-    vq = (tid / (D / 4)) & 7;
-    dq = tid % (D / 4);
-    v_off = (kvh * kBlock + 4 * (vq & 3)) * D + 4 * dq;
-  }
-};
-
-// Issue the global loads of a key tile.  Every load stays inside the pool;
-// rows past the context are fixed up by store_tile.
-template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D>& sg, const TileBlocks& tb,
-                                          const half_t* __restrict__ kc,
-                                          const half_t* __restrict__ vc, int64_t blk_stride,
-                                          int w) {
-  using G = PGeom<D>;
-#pragma unroll
-  for (int i = 0; i < G::KLOADS; ++i) {
-    const int blk = (i * kThreads + 64 * w) / (kBlock * G::CPR);  // wave-uniform
-    const half_t* base = kc + static_cast<int64_t>(pick_block(blk, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
-    st.k[i] = *reinterpret_cast<const u32x4_t*>(base + sg.k_off);
-  }
-  if (sg.v_on) {
-    // pair p = vq / 4 is wave-uniform: 64 threads cover 64 / (D/4) granules of one pair
-    const int p = __builtin_amdgcn_readfirstlane(sg.vq >> 2);
-    const half_t* b0 = vc + static_cast<int64_t>(pick_block(2 * p, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
-    const half_t* b1 = vc + static_cast<int64_t>(pick_block(2 * p + 1, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = *reinterpret_cast<const u32x2_t*>(b0 + sg.v_off + i * D);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[4 + i] = *reinterpret_cast<const u32x2_t*>(b1 + sg.v_off + i * D);
-  }
-}
-
-// Write a staged tile to one LDS buffer: K row-major, V transposed.  On the
-// tile holding the end of the keys (tail), V rows at or past n_keys are zeroed
-// (their P is 0, but stale cache rows may hold non-finite bits); K rows there
-// only produce scores that the causal mask removes.
-template <int D>
-__device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D>& sg, half_t* __restrict__ sK,
-                                           half_t* __restrict__ sVt, bool tail, int key0, int n_keys) {
-  using G = PGeom<D>;
-#pragma unroll
-  for (int i = 0; i < G::KLOADS; ++i) {
-    const int r = sg.k_row + i * (kThreads / G::CPR);
-    *reinterpret_cast<u32x4_t*>(&sK[r * D + ((sg.k_col ^ kswz<D>(r)) << 3)]) = st.k[i];
-  }
-  if (!sg.v_on) return;
-  if (tail) {
-    const int kb = key0 + 32 * (sg.vq >> 2) + 4 * (sg.vq & 3);
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-      if (kb + 16 * (s8 >> 2) + (s8 & 3) >= n_keys) st.v[s8] = u32x2_t{0u, 0u};
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // column 4 dq + j of the granule's 8 keys, two keys a word: half j & 1 of word j / 2
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    u32x4_t row;
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd)
-      row[wd] = __builtin_amdgcn_perm(st.v[2 * wd + 1][j >> 1], st.v[2 * wd][j >> 1], sel);
-    const int r = 4 * sg.dq + j;
-    *reinterpret_cast<u32x4_t*>(&sVt[r * kBk + ((sg.vq ^ swz8(r)) << 3)]) = row;
-  }
-}
-
-// grid (ceil(B * Hq / 8) * 8 * nqt), block 256.  qk_scale = softmax scale * log2 e.
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
-    const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
-    const int32_t* __restrict__ tables, float* __restrict__ out, int32_t B, int32_t Hq,
-    int32_t Hkv, int32_t total_q, int32_t max_blocks, int32_t num_blocks, int32_t nqt,
-    float qk_scale) {
-  using G = PGeom<D>;
-  __shared__ __attribute__((aligned(16))) half_t sK[2 * G::KBUF];
-  __shared__ __attribute__((aligned(16))) half_t sVt[2 * G::VBUF];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
-
-  // workgroup -> (query tile, pair): ids 8 apart share a pair, so one XCD
-  const int u = blockIdx.x;
-  const int x = u % kXcds;
-  const int rest = u / kXcds;
-  const int qt = rest % nqt;
-  const int pair = (rest / nqt) * kXcds + x;
-  if (pair >= B * Hq) return;
-  const int h = pair % Hq;
-  const int rank = pair / Hq;
-  int b;
-  if (B <= 64) {
-    int Wb = 0;
-    if (lane < B) Wb = max(prior[lane], 0) + (cu_q[lane + 1] - cu_q[lane]);
-    b = __ffsll(static_cast<unsigned long long>(__ballot(work_rank(Wb, lane, B) == rank))) - 1;
-  } else {
-    b = rank;
-  }
-
-  const int row0 = cu_q[b];
-  const int C = cu_q[b + 1] - row0;
-  const int P = max(prior[b], 0);
-  const int q0 = qt * kBq;
-  if (q0 >= C || row0 < 0) return;
-  const int L_total = min(P + C, max_blocks * kBlock);
-  const int kvh = h / (Hq / Hkv);
-  const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
-
-  // Scores are kept in raw units and scaled inside the exponent by c > 0; a
-  // negative scale flips the sign of q instead (exact).  A zero scale becomes
-  // 1e-30, which leaves every exp2 of a finite score at 1 and keeps masked
-  // scores at -inf (a zero factor would turn them into NaN).
-  const bool neg = qk_scale < 0.f;
-  const float c = fmaxf(neg ? -qk_scale : qk_scale, 1e-30f);
-
-  // Q as the B operand of S^T = K Q^T: lane holds q[row = c16][d = 32 kk + 8 g .. +8]
-  half8_t qb[2][G::DK];
-  int qrow[2];
-  bool qvalid[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    qrow[st] = q0 + 32 * w + 16 * st + c16;
-    qvalid[st] = qrow[st] < C && (row0 + qrow[st]) < total_q;
-    const half_t* qp = q + (static_cast<int64_t>(row0 + qrow[st]) * Hq + h) * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < G::DK; ++kk) {
-      half8_t v = qvalid[st] ? *reinterpret_cast<const half8_t*>(qp + 32 * kk) : half8_t{};
-      qb[st][kk] = neg ? -v : v;
-    }
-  }
-
-  float4_t o[2][G::DT];
-  float m[2], l[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    m[st] = -INFINITY;
-    l[st] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < G::DT; ++dt) o[st][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int wq_first = q0 + 32 * w;                      // first query row of this wave
-  const int wq_last = min(q0 + 32 * w + 32, C) - 1;      // last valid one (< first if none)
-  const int n_keys = min(P + min(q0 + kBq, C), L_total);  // keys any row of the group needs
-  const int ntiles = (n_keys + kBk - 1) / kBk;
-
-  StageGeom<D> sg;
-  sg.init(tid, kvh);
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * kBlock * D;
-  Stage<D> stg;
-  int ids_next = 0;
-  if (ntiles > 0) {
-    load_tile<D>(stg, sg, tile_blocks(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
-    ids_next = tile_ids_lanes(trow, 1, max_blocks, lane);
-    store_tile<D>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
-  }
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int key0 = kt * kBk;
-    const bool more = kt + 1 < ntiles;
-    if (more) {
-      const TileBlocks tb = tile_blocks_from(ids_next, num_blocks);
-      ids_next = tile_ids_lanes(trow, kt + 2, max_blocks, lane);
-      load_tile<D>(stg, sg, tb, kc, vc, blk_stride, w);
-    }
-    __syncthreads();  // buffer kt % 2 written; buffer (kt + 1) % 2 no longer read
-    const half_t* cK = sK + (kt & 1) * G::KBUF;
-    const half_t* cVt = sVt + (kt & 1) * G::VBUF;
-
-    if (!(wq_last < wq_first || key0 > P + wq_last)) {  // keys of this tile visible to the wave
-      // S^T tiles: [st][ks] holds keys key0 + 16 ks + 4 g + i for query row c16
-      float4_t sacc[2][4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sacc[st][ks] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < G::DK; ++kk) {
-        half8_t a[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          a[ks] = *reinterpret_cast<const half8_t*>(
-              &cK[(ks * 16 + c16) * D + (((4 * kk + g) ^ kswz<D>(ks * 16 + c16)) << 3)]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            sacc[st][ks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], qb[st][kk], sacc[st][ks], 0, 0, 0);
-      }
-
-      if (key0 + kBk - 1 > P + wq_first) {  // tile crosses the diagonal of some row
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int lim = P + qrow[st];  // last visible key of this lane's row
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (key0 + 16 * ks + 4 * g + i > lim) sacc[st][ks][i] = -INFINITY;
-        }
-      }
-
-      half_t ph[2][4][4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float mt = -INFINITY;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          mt = fmaxf(mt, fmaxf(fmaxf(sacc[st][ks][0], sacc[st][ks][1]),
-                               fmaxf(sacc[st][ks][2], sacc[st][ks][3])));
-        // move the running max (and rescale) only when some lane's scores grew
-        // past it by more than 2^kLazyRescale: exp2 arguments stay <=
-        // kLazyRescale.  The lane-local max decides; the row max over the 4
-        // lane groups is only formed when a rescale happens.
-        const float grow = (mt - m[st]) * c;  // +inf on the first visible tile
-        if (__ballot(grow > kLazyRescale) != 0) {
-          mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-          const float m_new = fmaxf(m[st], mt);
-          const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2((m[st] - m_new) * c);
-          l[st] *= corr;
-#pragma unroll
-          for (int dt = 0; dt < G::DT; ++dt) o[st][dt] *= corr;
-          m[st] = m_new;
-        }
-        const float mc = (m[st] == -INFINITY) ? 0.f : m[st] * c;
-        float ps = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pr = fast_exp2(fmaf(sacc[st][ks][i], c, -mc));
-            ps += pr;
-            ph[st][ks][i] = static_cast<half_t>(pr);
-          }
-        }
-        l[st] += ps;
-      }
-
-      // O^T += V^T P^T over two 32-key pairs of sub-tiles (0,1) and (2,3)
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        half8_t bp[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          bp[st] = half8_t{ph[st][2 * kp][0], ph[st][2 * kp][1], ph[st][2 * kp][2], ph[st][2 * kp][3],
-                           ph[st][2 * kp + 1][0], ph[st][2 * kp + 1][1], ph[st][2 * kp + 1][2],
-                           ph[st][2 * kp + 1][3]};
-        }
-#pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt) {
-          const int vr = dt * 16 + c16;
-          const half8_t a =
-              *reinterpret_cast<const half8_t*>(&cVt[vr * kBk + (((kp * 4 + g) ^ swz8(vr)) << 3)]);
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            o[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[st], o[st][dt], 0, 0, 0);
-        }
-      }
-    }
-    if (more)
-      store_tile<D>(stg, sg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF,
-                    key0 + 2 * kBk > n_keys, key0 + kBk, n_keys);
-  }
-
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    float lt = l[st];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (!qvalid[st]) continue;
-    const float inv = 1.0f / lt;
-    float* orow = out + (static_cast<int64_t>(row0 + qrow[st]) * Hq + h) * D + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < G::DT; ++dt) {
-      *reinterpret_cast<float4_t*>(orow + dt * 16) = o[st][dt] * inv;
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,

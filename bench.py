@@ -94,12 +94,24 @@ def fp8_scales(w, np):
     return float(np.float32(ka / np.float32(448))), float(np.float32(va / np.float32(448)))
 
 
-def setup_decode(w, fp8: bool, pa, torch, np):
+def pool_geometry(w, block_size, np):
+    """(num_blocks, free order) holding ``w``'s tokens at ``block_size``: the
+    workloads size their pools in 16-token blocks; other sizes keep the
+    capacity in tokens plus one spare block per sequence, freshly shuffled."""
+    if block_size == 16:
+        return w.num_blocks, w.init_free_order
+    nb = -(-w.num_blocks * 16 // block_size) + w.batch + 8
+    return nb, np.random.default_rng(1000 + w.seed + block_size).permutation(nb).astype(np.int32)
+
+
+def setup_decode(w, fp8: bool, pa, torch, np, block_size=16):
     """Admit every sequence with its context minus the newest token, write that
     KV, then allocate the newest token (the step's write target)."""
-    pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
+    nb, order = pool_geometry(w, block_size, np)
+    pool = pa.pa_pool_create(nb, block_size, order)
     ks, vs = fp8_scales(w, np) if fp8 else (1.0, 1.0)
-    cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim, fp8=fp8, k_scale=ks, v_scale=vs)
+    cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size, fp8=fp8, k_scale=ks,
+                       v_scale=vs)
     ids, new_k, new_v, new_slots = [], [], [], []
     t_alloc = 0.0
     for b in range(w.batch):
@@ -121,7 +133,7 @@ def setup_decode(w, fp8: bool, pa, torch, np):
         new_slots.append(int(slots[0]))
     t_step_alloc = time.perf_counter() - t0
     max_ctx = int(w.lens.max())
-    max_blocks = -(-max_ctx // 16)
+    max_blocks = -(-max_ctx // block_size)
     t0 = time.perf_counter()
     tables, lens = pa.pa_block_tables(pool, ids, max_blocks)
     t_export = time.perf_counter() - t0
@@ -188,14 +200,14 @@ def run_decode(pa, torch, w, d, steps, warmup):
     return 1e3 * (t1 - t0) / steps, mean_dec, dec_ms[len(dec_ms) // 2]
 
 
-def decode_bytes(w, elem_bytes, lens=None):
+def decode_bytes(w, elem_bytes, lens=None, block_size=16):
     """Algorithmic bytes of one pa_decode: K and V rows of every cached token
     read once, q read, fp32 output written, block tables and lengths read
     (split partials, when used, are not algorithmic)."""
     lens = w.lens if lens is None else lens
     kv = int(lens.sum()) * w.num_kv_heads * w.head_dim * 2 * elem_bytes
     io = w.batch * w.num_heads * w.head_dim * (2 + 4)
-    tables = w.batch * (-(-int(lens.max()) // 16)) * 4 + w.batch * 4
+    tables = w.batch * (-(-int(lens.max()) // block_size)) * 4 + w.batch * 4
     return kv, kv + io + tables
 
 
@@ -409,10 +421,11 @@ def bench_mixed(pa, torch, np, workloads, reps):
             "speedup": round(sep_ms / mixed_ms, 3)}
 
 
-def bench_prefill(pa, torch, np, workloads, reps):
+def bench_prefill(pa, torch, np, workloads, reps, block_size=16):
     w = workloads.chunked_prefill()
-    pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
-    cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim)
+    nb, order = pool_geometry(w, block_size, np)
+    pool = pa.pa_pool_create(nb, block_size, order)
+    cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size)
     ids = []
     for b in range(w.batch):
         s = pa.pa_seq_create(pool)
@@ -425,7 +438,7 @@ def bench_prefill(pa, torch, np, workloads, reps):
                 pa.pa_write_kv(cache, torch.from_numpy(np.ascontiguousarray(k[lo:lo + n])).cuda(),
                                torch.from_numpy(np.ascontiguousarray(v[lo:lo + n])).cuda(),
                                torch.from_numpy(slots).cuda())
-    max_blocks = -(-int(w.lens.max()) // 16)
+    max_blocks = -(-int(w.lens.max()) // block_size)
     tables, _ = pa.pa_block_tables(pool, ids, max_blocks)
     tables = torch.from_numpy(tables).cuda()
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(w.chunk)]).astype(np.int32)).cuda()
@@ -443,6 +456,31 @@ def bench_prefill(pa, torch, np, workloads, reps):
             "causal_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
             "mfma_util": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
             "peak_tflops": MFMA_F16_PEAK_TFLOPS}
+
+
+def bench_block_sizes(pa, torch, np, workloads, w, steps, warmup, at16):
+    """The 13B decode batch and the chunked-prefill batch at block sizes 8 and
+    32 (16 is the headline line): pa_decode bandwidth, the slots lost to
+    partly filled last blocks, and prefill time."""
+    res = {}
+    for bs in (8, 16, 32):
+        if bs == 16:
+            d_ms, p_ms = at16
+        else:
+            d = setup_decode(w, False, pa, torch, np, block_size=bs)
+            _, d_ms, _ = run_decode(pa, torch, w, d, steps, warmup)
+            del d
+            torch.cuda.empty_cache()
+            p_ms = bench_prefill(pa, torch, np, workloads, 20, block_size=bs)["ms"]
+        _, alg = decode_bytes(w, 2, block_size=bs)
+        blocks = int(np.sum(-(-w.lens // bs)))
+        res[str(bs)] = {"pa_decode_ms": round(d_ms, 5),
+                        "pa_decode_gbs": round(alg / (d_ms * 1e-3) / 1e9, 2),
+                        "hbm_frac": round(alg / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "blocks": blocks, "waste_tokens": blocks * bs - int(w.lens.sum()),
+                        "waste_frac": round(1.0 - int(w.lens.sum()) / (blocks * bs), 5),
+                        "prefill_ms": round(p_ms, 4)}
+    return {"workload": "llama13b_decode (64 seqs, fp16) and chunked_prefill (8 x 512 rows)", **res}
 
 
 def cpu_baseline(w, np, target_s=15.0):
@@ -660,6 +698,10 @@ def main():
         torch.cuda.empty_cache()
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
+        torch.cuda.empty_cache()
+        log("block sizes 8 / 32")
+        res["block_sizes"] = bench_block_sizes(pa, torch, np, workloads, w, args.steps, args.warmup,
+                                               (dec_ms, res["prefill"]["ms"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, np, args.cpu_seconds)

@@ -26,11 +26,15 @@ pa_status check_cache(const pa_kv_cache* c, const char* fn, pa::KvDesc* d) {
     return fail(PA_ERR_BAD_ARG, f + ": caches must be 16-byte aligned");
   if (c->num_blocks < 1 || c->num_kv_heads < 1)
     return fail(PA_ERR_BAD_ARG, f + ": num_blocks and num_kv_heads must be >= 1");
-  if (static_cast<int64_t>(c->num_blocks) * 16 >= (int64_t(1) << 31))
-    return fail(PA_ERR_BAD_ARG, f + ": num_blocks * 16 must be < 2^31");
-  if (c->block_size != 16) return fail(PA_ERR_UNSUPPORTED, f + ": kernels are built for block_size 16");
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, f + ": kernels are built for block_size 8, 16 and 32");
+  if (static_cast<int64_t>(c->num_blocks) * c->block_size >= (int64_t(1) << 31))
+    return fail(PA_ERR_BAD_ARG, f + ": num_blocks * block_size must be < 2^31");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (c->dtype == PA_KV_FP8_E4M3 && c->block_size * c->head_dim < 1024)
+    return fail(PA_ERR_UNSUPPORTED, f + ": an e4m3 (block, head) tile must be at least 1 KiB "
+                                        "(block_size 8 needs head_dim 128)");
   if (c->dtype != PA_KV_F16 && c->dtype != PA_KV_FP8_E4M3)
     return fail(PA_ERR_BAD_ARG, f + ": unknown cache dtype");
   const bool fp8 = c->dtype == PA_KV_FP8_E4M3;
@@ -194,7 +198,7 @@ pa_status pa_mixed_step(const pa_kv_cache* cache, int32_t num_heads, float scale
       return st;
   }
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (has_p && has_d && decode->max_context_len <= pa::mixed_max_context()) {
+  if (has_p && has_d && decode->max_context_len <= pa::mixed_max_context(d.block_size)) {
     const pa::MixedPrefill mp{prefill->q, prefill->total_q, prefill->cu_q, prefill->prior,
                               prefill->tables, prefill->batch, prefill->max_blocks,
                               prefill->max_chunk, prefill->out};

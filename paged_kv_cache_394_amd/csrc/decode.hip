@@ -1,5 +1,6 @@
 // Paged decode attention for gfx950: one query per (sequence, head) over a KV
-// cache scattered across 16-token physical blocks found through a block table
+// cache scattered across physical blocks of 8, 16 or 32 tokens found through a
+// block table
 // ([p1] "vLLM PagedAttention Deep Dive", section "PagedAttention Mechanism":
 // look up the physical blocks, gather their K/V, run standard attention).
 //
@@ -13,7 +14,8 @@
 // * The block-table entries of the run are read once, one per lane, and each
 //   block id is then taken with a lane read into a scalar register, so no
 //   dependent memory access sits inside the block loop.
-// * Coalesced tiles.  One (block, head) tile is 16 x head_dim contiguous values.
+// * Coalesced tiles.  One (block, head) tile is block_size x head_dim contiguous
+//   values (at least 1 KiB: fp16, or e4m3 with block_size * head_dim >= 1024).
 //   Load instruction i of a wave reads bytes [1024 i, 1024 i + 1024) of the tile,
 //   16 bytes per lane, so each load is one fully used 1 KiB run.  A lane then
 //   holds 16 bytes of one token row; the lanes of one row (head_dim*bytes/16 of
@@ -66,12 +68,12 @@ struct UnitPos {
 // then the one partly filled split of each sequence sorted by size, largest
 // first (ties by sequence index), and last a zero-size unit for each empty
 // context, which writes its zero output.
-template <int kSplit>
+template <int kSplit, int BS>
 __device__ __forceinline__ UnitPos longest_first_unit(int f, const int32_t* __restrict__ lens,
                                                       int B, int ctx_cap, int lane) {
   int Lb = 0;
   if (lane < B) Lb = min(max(lens[lane], 0), ctx_cap);
-  const int nblk = (Lb + kBlock - 1) / kBlock;
+  const int nblk = (Lb + BS - 1) / BS;
   const int F = nblk / kSplit;      // full splits
   const int psz = nblk % kSplit;    // blocks in the partly filled split (0: none)
   const bool has_tail = lane < B && (psz != 0 || nblk == 0);
@@ -115,9 +117,9 @@ __device__ __forceinline__ UnitPos longest_first_unit(int f, const int32_t* __re
 // grid (ceil(units / kWPG)), block kWPG * 64.  With kLongestFirst (B <= 64) the
 // units follow longest_first_unit; otherwise unit u = (split * B + b) * Hq + h.
 //   qk_scale = softmax scale * log2(e) * k_scale;  v_scale = 1 for fp16.
-//   ctx_cap = min(max_blocks * 16, max_context_len): lengths are clamped to it.
+//   ctx_cap = min(max_blocks * BS, max_context_len): lengths are clamped to it.
 //   ws_o [B][Hq][nsplit][D], ws_ml [B][Hq][nsplit][2] (max, sum), log2 domain.
-template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst>
+template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst, int BS>
 __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
     const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
     float* __restrict__ ws_ml, int32_t B, int32_t Hq, int32_t Hkv,
     int32_t max_blocks, int32_t ctx_cap, int32_t nsplit, int32_t num_blocks, float qk_scale,
     float v_scale) {
-  using G = Geom<D, FP8>;
+  using G = Geom<D, FP8, BS>;
   static_assert(kSplit % kU == 0, "a split is a whole number of steps");
   constexpr int kTR = (kSplit + 63) / 64;  // block-id registers per lane
   const int lane = threadIdx.x & 63;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
   const int h = unit % Hq;
   int b, split, L;
   if constexpr (kLongestFirst) {
-    const UnitPos pos = longest_first_unit<kSplit>(unit / Hq, lens, B, ctx_cap, lane);
+    const UnitPos pos = longest_first_unit<kSplit, BS>(unit / Hq, lens, B, ctx_cap, lane);
     if (!pos.valid) return;
     b = pos.b;
     split = pos.split;
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
   qr.load(q + bh * D + col * G::kEpl);
 
   L = min(max(L, 0), ctx_cap);
-  const int nblk = (L + kBlock - 1) / kBlock;
+  const int nblk = (L + BS - 1) / BS;
   if (blk0 >= nblk) {
     if (split == 0) {  // empty context: zero output
       for (int d = lane; d < D; d += 64) out[bh * D + d] = 0.f;
@@ -175,9 +177,9 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
   const uint8_t* vb = vc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
   const int64_t stride = static_cast<int64_t>(Hkv) * G::kTile;
   if (cached != nullptr && blk0 < cached[b])
-    stream_blocks<D, FP8, kU, kPipe, kTR, false>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+    stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
   else
-    stream_blocks<D, FP8, kU, kPipe, kTR, true>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+    stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
   const float l = sum_rows<D, FP8>(sm);
   if (row != 0) return;
   float* dst;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
                                                             const int32_t* __restrict__ lens,
                                                             float* __restrict__ out, int32_t B,
                                                             int32_t Hq, int32_t ctx_cap,
-                                                            int32_t nsplit, int32_t split_blocks) {
+                                                            int32_t nsplit, int32_t split_tokens) {
   constexpr int kCols = D / 64;
   const int lane = threadIdx.x & 63;
   const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -234,8 +236,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
     }
   }
   L = min(max(L, 0), ctx_cap);
-  const int nblk = (L + kBlock - 1) / kBlock;
-  const int np = (nblk + split_blocks - 1) / split_blocks;
+  const int np = (L + split_tokens - 1) / split_tokens;
   if (np <= 1) return;
   float M = -INFINITY;
 #pragma unroll
@@ -270,26 +271,31 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ out, int6
   if (i < n) out[i] = 0.f;
 }
 
-int64_t ctx_blocks_of(int32_t max_ctx) { return (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock; }
+int64_t ctx_blocks_of(int32_t max_ctx, int bs) { return (static_cast<int64_t>(max_ctx) + bs - 1) / bs; }
 
-int32_t ctx_cap_of(int32_t max_blocks, int32_t max_ctx) {
-  return static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(max_blocks) * kBlock, max_ctx));
+int32_t ctx_cap_of(int32_t max_blocks, int32_t max_ctx, int bs) {
+  return static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(max_blocks) * bs, max_ctx));
 }
 
-template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst>
+// Splits cover kSplitTokens tokens whatever the block size, so the workspace
+// (one partial per split) does not depend on it.
+constexpr int kSplitTokens = 512;
+
+template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst, int BS>
 hipError_t run_split(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                      const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
                      int32_t max_ctx, float scale, float* out, void* workspace, hipStream_t s) {
-  const int64_t nsplit64 = (ctx_blocks_of(max_ctx) + kSplit - 1) / kSplit;
+  static_assert(kSplit * BS == kSplitTokens, "a split is kSplitTokens tokens");
+  const int64_t nsplit64 = (ctx_blocks_of(max_ctx, BS) + kSplit - 1) / kSplit;
   const int32_t nsplit = static_cast<int32_t>(nsplit64);
   const int64_t units = nsplit64 * B * Hq;
-  const int32_t ctx_cap = ctx_cap_of(max_blocks, max_ctx);
+  const int32_t ctx_cap = ctx_cap_of(max_blocks, max_ctx, BS);
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o + static_cast<size_t>(B) * Hq * nsplit * D;
   const float qk_scale = scale * kLog2e * (FP8 ? c.k_scale : 1.0f);
   const float v_scale = FP8 ? c.v_scale : 1.0f;
   const uint32_t groups = static_cast<uint32_t>((units + kWPG - 1) / kWPG);
-  decode_split_kernel<D, FP8, kSplit, kU, kPipe, kWPG, kLongestFirst>
+  decode_split_kernel<D, FP8, kSplit, kU, kPipe, kWPG, kLongestFirst, BS>
       <<<dim3(groups), dim3(kWPG * 64), 0, s>>>(
           static_cast<const half_t*>(q), static_cast<const uint8_t*>(c.k),
           static_cast<const uint8_t*>(c.v), tables, lens, cached, out, ws_o, ws_ml, B, Hq,
@@ -300,36 +306,35 @@ hipError_t run_split(const KvDesc& c, const void* q, int32_t Hq, const int32_t* 
   if (nsplit > 1) {
     const uint32_t rgroups = static_cast<uint32_t>((static_cast<int64_t>(B) * Hq + 3) / 4);
     decode_reduce_kernel<D, 8><<<dim3(rgroups), dim3(256), 0, s>>>(ws_o, ws_ml, lens, out, B, Hq,
-                                                                   ctx_cap, nsplit, kSplit);
+                                                                   ctx_cap, nsplit, kSplitTokens);
     e = hipGetLastError();
   }
   return e;
 }
 
-template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR>
+template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
 hipError_t run_seq(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                    const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
                    int32_t max_ctx, float scale, float* out, hipStream_t s) {
   const float qk_scale = scale * kLog2e * (FP8 ? c.k_scale : 1.0f);
   const float v_scale = FP8 ? c.v_scale : 1.0f;
-  decode_seq_kernel<D, FP8, kU, kPipe, kW, kTR>
+  decode_seq_kernel<D, FP8, kU, kPipe, kW, kTR, BS>
       <<<dim3(static_cast<uint32_t>(static_cast<int64_t>(B) * Hq)), dim3(kW * 64), 0, s>>>(
           static_cast<const half_t*>(q), static_cast<const uint8_t*>(c.k),
           static_cast<const uint8_t*>(c.v), tables, lens, cached, out, B, Hq, c.num_kv_heads,
-          max_blocks, ctx_cap_of(max_blocks, max_ctx), c.num_blocks, qk_scale, v_scale);
+          max_blocks, ctx_cap_of(max_blocks, max_ctx, BS), c.num_blocks, qk_scale, v_scale);
   return hipGetLastError();
 }
 
-// Launch configurations.  Split path: blocks per split, blocks per step,
-// pipelined, waves per workgroup.  Per-sequence path: blocks per step,
-// pipelined, waves per workgroup (4, or 8 for batches too small to fill the
-// chip with 4), block-id registers per wave (a wave takes at most 64 * kSeqTR
-// blocks).
-constexpr int kSplitF16 = 32, kUF16 = 2, kWpgF16 = 2;
+// Launch configurations.  Split path: blocks per step, pipelined, waves per
+// workgroup (a split is kSplitTokens tokens).  Per-sequence path: blocks per
+// step, pipelined, waves per workgroup (4, or 8 for batches too small to fill
+// the chip with 4), block-id registers per wave (a wave takes at most
+// 64 * kSeqTR blocks).
+constexpr int kUF16 = 2, kWpgF16 = 2;
 constexpr bool kPipeF16 = true;
-constexpr int kSplitF8 = 32, kUF8 = 4, kWpgF8 = 1;
+constexpr int kUF8 = 4, kWpgF8 = 1;
 constexpr bool kPipeF8 = false;
-static_assert(kSplitF16 == kSplitF8, "one split size: the workspace size does not depend on dtype");
 constexpr int kSeqUF16 = 2, kSeqUF8 = 4;
 constexpr bool kSeqPipeF16 = false, kSeqPipeF8 = false;
 constexpr int kSeqTR = 1;
@@ -340,27 +345,74 @@ constexpr int64_t kSeqMinWaves = 8192;
 
 // Waves per workgroup of the per-sequence path for this batch, or 0 for the
 // split path.
-int seq_waves(int32_t B, int32_t Hq, int32_t max_ctx) {
+int seq_waves(int32_t B, int32_t Hq, int32_t max_ctx, int bs) {
   const int64_t pairs = static_cast<int64_t>(B) * Hq;
-  const int64_t blocks = ctx_blocks_of(max_ctx);
+  const int64_t blocks = ctx_blocks_of(max_ctx, bs);
   for (int w : {4, 8}) {
     if (pairs * w >= kSeqMinWaves && (blocks + w - 1) / w <= 64 * kSeqTR) return w;
   }
   return 0;
 }
 
+// A (block, head) tile must cover at least one 1 KiB wave load.
+template <int D, bool FP8, int BS>
+constexpr bool kTileFits = BS * D * (FP8 ? 1 : 2) >= 1024;
+
+template <int D, bool FP8, int BS>
+hipError_t launch_decode_typed(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
+                               const int32_t* lens, const int32_t* cached, int32_t B,
+                               int32_t max_blocks, int32_t max_ctx, float scale, float* out,
+                               void* workspace, hipStream_t s) {
+  if constexpr (!kTileFits<D, FP8, BS>) {
+    return hipErrorInvalidValue;  // rejected by the caller's argument checks
+  } else {
+    constexpr int kU = FP8 ? kSeqUF8 : kSeqUF16;
+    constexpr bool kPipe = FP8 ? kSeqPipeF8 : kSeqPipeF16;
+    const int sw = seq_waves(B, Hq, max_ctx, BS);
+    if (sw == 4)
+      return run_seq<D, FP8, kU, kPipe, 4, kSeqTR, BS>(c, q, Hq, tables, lens, cached, B, max_blocks,
+                                                       max_ctx, scale, out, s);
+    if (sw == 8)
+      return run_seq<D, FP8, kU, kPipe, 8, kSeqTR, BS>(c, q, Hq, tables, lens, cached, B, max_blocks,
+                                                       max_ctx, scale, out, s);
+    constexpr int kSplit = kSplitTokens / BS;
+    constexpr int kSU = FP8 ? kUF8 : kUF16;
+    constexpr bool kSPipe = FP8 ? kPipeF8 : kPipeF16;
+    constexpr int kWpg = FP8 ? kWpgF8 : kWpgF16;
+    // longest-first unit order needs every length in one wave: B <= 64
+    if (B <= 64)
+      return run_split<D, FP8, kSplit, kSU, kSPipe, kWpg, true, BS>(
+          c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s);
+    return run_split<D, FP8, kSplit, kSU, kSPipe, kWpg, false, BS>(
+        c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s);
+  }
+}
+
+template <int BS>
+hipError_t launch_decode_bs(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
+                            const int32_t* lens, const int32_t* cached, int32_t B,
+                            int32_t max_blocks, int32_t max_ctx, float scale, float* out,
+                            void* workspace, hipStream_t s) {
+#define PA_ARGS c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s
+  if (c.head_dim == 128)
+    return c.fp8 ? launch_decode_typed<128, true, BS>(PA_ARGS)
+                 : launch_decode_typed<128, false, BS>(PA_ARGS);
+  return c.fp8 ? launch_decode_typed<64, true, BS>(PA_ARGS) : launch_decode_typed<64, false, BS>(PA_ARGS);
+#undef PA_ARGS
+}
+
 }  // namespace
 
-int32_t decode_partition_tokens() { return kSplitF16 * kBlock; }
+int32_t decode_partition_tokens() { return kSplitTokens; }
 
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len) {
   if (B <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0) return 0;
-  const int64_t nsplit = (ctx_blocks_of(max_context_len) + kSplitF16 - 1) / kSplitF16;
+  const int64_t nsplit = (static_cast<int64_t>(max_context_len) + kSplitTokens - 1) / kSplitTokens;
   return static_cast<size_t>(B) * Hq * nsplit * (D + 2) * sizeof(float);
 }
 
 int64_t decode_units(int32_t B, int32_t Hq, int32_t max_context_len) {
-  const int64_t nsplit = (ctx_blocks_of(max_context_len) + kSplitF16 - 1) / kSplitF16;
+  const int64_t nsplit = (static_cast<int64_t>(max_context_len) + kSplitTokens - 1) / kSplitTokens;
   return nsplit * B * Hq;
 }
 
@@ -374,39 +426,17 @@ hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32
     zero_kernel<<<dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s>>>(out, n);
     return hipGetLastError();
   }
-#define PA_SEQ_ARGS c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, s
-#define PA_SPLIT_ARGS c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s
-  const int sw = seq_waves(B, Hq, max_ctx);
-  if (sw == 4) {
-    if (c.head_dim == 128)
-      return c.fp8 ? run_seq<128, true, kSeqUF8, kSeqPipeF8, 4, kSeqTR>(PA_SEQ_ARGS)
-                   : run_seq<128, false, kSeqUF16, kSeqPipeF16, 4, kSeqTR>(PA_SEQ_ARGS);
-    return c.fp8 ? run_seq<64, true, kSeqUF8, kSeqPipeF8, 4, kSeqTR>(PA_SEQ_ARGS)
-                 : run_seq<64, false, kSeqUF16, kSeqPipeF16, 4, kSeqTR>(PA_SEQ_ARGS);
+  switch (c.block_size) {
+    case 8:
+      return launch_decode_bs<8>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
+                                 workspace, s);
+    case 32:
+      return launch_decode_bs<32>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
+                                  workspace, s);
+    default:
+      return launch_decode_bs<16>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
+                                  workspace, s);
   }
-  if (sw == 8) {
-    if (c.head_dim == 128)
-      return c.fp8 ? run_seq<128, true, kSeqUF8, kSeqPipeF8, 8, kSeqTR>(PA_SEQ_ARGS)
-                   : run_seq<128, false, kSeqUF16, kSeqPipeF16, 8, kSeqTR>(PA_SEQ_ARGS);
-    return c.fp8 ? run_seq<64, true, kSeqUF8, kSeqPipeF8, 8, kSeqTR>(PA_SEQ_ARGS)
-                 : run_seq<64, false, kSeqUF16, kSeqPipeF16, 8, kSeqTR>(PA_SEQ_ARGS);
-  }
-  // longest-first unit order needs every length in one wave: B <= 64
-  const bool lf = B <= 64;
-  if (c.head_dim == 128) {
-    if (c.fp8)
-      return lf ? run_split<128, true, kSplitF8, kUF8, kPipeF8, kWpgF8, true>(PA_SPLIT_ARGS)
-                : run_split<128, true, kSplitF8, kUF8, kPipeF8, kWpgF8, false>(PA_SPLIT_ARGS);
-    return lf ? run_split<128, false, kSplitF16, kUF16, kPipeF16, kWpgF16, true>(PA_SPLIT_ARGS)
-              : run_split<128, false, kSplitF16, kUF16, kPipeF16, kWpgF16, false>(PA_SPLIT_ARGS);
-  }
-  if (c.fp8)
-    return lf ? run_split<64, true, kSplitF8, kUF8, kPipeF8, kWpgF8, true>(PA_SPLIT_ARGS)
-              : run_split<64, true, kSplitF8, kUF8, kPipeF8, kWpgF8, false>(PA_SPLIT_ARGS);
-  return lf ? run_split<64, false, kSplitF16, kUF16, kPipeF16, kWpgF16, true>(PA_SPLIT_ARGS)
-            : run_split<64, false, kSplitF16, kUF16, kPipeF16, kWpgF16, false>(PA_SPLIT_ARGS);
-#undef PA_SPLIT_ARGS
-#undef PA_SEQ_ARGS
 }
 
 }  // namespace pa

@@ -13,16 +13,17 @@ namespace {
 
 using namespace dev;
 
-template <int D, bool FP8>
+// Layout of one (block, head) tile of BS tokens for the wave's loads.
+template <int D, bool FP8, int BS = 16>
 struct Geom {
   static constexpr int kBytes = FP8 ? 1 : 2;
   static constexpr int kEpl = 16 / kBytes;      // values per lane per 16-byte load
   static constexpr int kLpr = D / kEpl;         // lanes per token row
   static constexpr int kRpi = 64 / kLpr;        // token rows per 1 KiB load
-  static constexpr int kIpb = kBlock / kRpi;    // loads per block tile
-  static constexpr int kTile = kBlock * D * kBytes;
+  static constexpr int kIpb = BS / kRpi;        // loads per block tile
+  static constexpr int kTile = BS * D * kBytes;
   static_assert(kLpr >= 4 && kLpr <= 16, "row group must fit a DPP row");
-  static_assert(kIpb >= 1, "tile smaller than one load");
+  static_assert(kIpb >= 1 && BS % kRpi == 0, "tile smaller than one load");
 };
 
 // q . k for the lane's kEpl values.
@@ -101,10 +102,10 @@ __device__ __forceinline__ void axpy<true>(float* acc, float p, const u32x4_t& v
 }
 
 // K and V tiles of kU blocks held in registers.
-template <int D, bool FP8, int kU>
+template <int D, bool FP8, int kU, int BS>
 struct Tiles {
-  u32x4_t k[kU][Geom<D, FP8>::kIpb];
-  u32x4_t v[kU][Geom<D, FP8>::kIpb];
+  u32x4_t k[kU][Geom<D, FP8, BS>::kIpb];
+  u32x4_t v[kU][Geom<D, FP8, BS>::kIpb];
 };
 
 // Running state of one wave's online softmax.
@@ -150,16 +151,16 @@ __device__ __forceinline__ u32x4_t load_kv(const uint8_t* p) {
 // past L are masked).  kbase / vbase point at the (block 0, kv head) tile plus
 // the lane's 16-byte offset.  Leaves the online-softmax state in sm.  kNT
 // picks the load flavour (load_kv).
-template <int D, bool FP8, int kU, bool kPipe, int kTR, bool kNT>
+template <int D, bool FP8, int kU, bool kPipe, int kTR, bool kNT, int BS>
 __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&tb)[kTR], int nb,
                                               int blk0, int L, const uint8_t* kbase,
                                               const uint8_t* vbase, int64_t blk_stride,
                                               float qk_scale, int row, Softmax<D, FP8>& sm) {
-  using G = Geom<D, FP8>;
+  using G = Geom<D, FP8, BS>;
 
   // Issue the loads of blocks j .. j+kU-1 of the run (past-the-end slots
   // reload the last block and are masked when consumed).
-  auto issue = [&](Tiles<D, FP8, kU>& t, int j) {
+  auto issue = [&](Tiles<D, FP8, kU, BS>& t, int j) {
     int64_t off[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -182,7 +183,7 @@ __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&t
         t.v[u][i] = load_kv<kNT>(vbase + off[u] + i * 1024);
   };
 
-  auto consume = [&](Tiles<D, FP8, kU>& t, int j) {
+  auto consume = [&](Tiles<D, FP8, kU, BS>& t, int j) {
     float s[kU][G::kIpb];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -190,12 +191,12 @@ __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&t
       for (int i = 0; i < G::kIpb; ++i) s[u][i] = group_sum<G::kLpr>(qr.dot(t.k[u][i])) * qk_scale;
     // Only the step holding the end of the run or of the context has rows to
     // mask (tokens at or past L, past-the-end block slots): a uniform branch.
-    if (j + kU > nb || (blk0 + j + kU) * kBlock > L) {
+    if (j + kU > nb || (blk0 + j + kU) * BS > L) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
 #pragma unroll
         for (int i = 0; i < G::kIpb; ++i) {
-          const int tok = (blk0 + j + u) * kBlock + i * G::kRpi + row;
+          const int tok = (blk0 + j + u) * BS + i * G::kRpi + row;
           if (!((j + u < nb) && (tok < L))) {
             s[u][i] = -INFINITY;
             t.v[u][i] = u32x4_t{0u, 0u, 0u, 0u};  // stale rows may hold non-finite bits
@@ -230,7 +231,7 @@ __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&t
   if constexpr (kPipe) {
     // two register buffers: the loads of one step are in flight while the
     // other is consumed
-    Tiles<D, FP8, kU> ta, tb2;
+    Tiles<D, FP8, kU, BS> ta, tb2;
     issue(ta, 0);
     for (int j = 0;; j += 2 * kU) {
       const bool more1 = j + kU < nb;
@@ -244,7 +245,7 @@ __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&t
     }
   } else {
     for (int j = 0; j < nb; j += kU) {
-      Tiles<D, FP8, kU> t;
+      Tiles<D, FP8, kU, BS> t;
       issue(t, j);
       consume(t, j);
     }
@@ -281,13 +282,13 @@ __device__ __forceinline__ int length_rank(int Lb, int lane, int B) {
 // sequences keep their index order).  Wave w streams blocks
 // [w nblk / kW, (w + 1) nblk / kW) of the context; at most 64 * kTR blocks per
 // wave (checked by the host).
-template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR>
+template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
 __device__ __forceinline__ void decode_seq_body(
     int g, const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cached, float* __restrict__ out, int32_t B, int32_t Hq, int32_t Hkv,
     int32_t max_blocks, int32_t ctx_cap, int32_t num_blocks, float qk_scale, float v_scale) {
-  using G = Geom<D, FP8>;
+  using G = Geom<D, FP8, BS>;
   static_assert(kW >= 2 && kW <= 8, "2 to 8 waves per workgroup");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -308,7 +309,7 @@ __device__ __forceinline__ void decode_seq_body(
   const int kvh = h / (Hq / Hkv);
   const int col = lane % G::kLpr;
   const int row = lane / G::kLpr;
-  const int nblk = (L + kBlock - 1) / kBlock;
+  const int nblk = (L + BS - 1) / BS;
   const int blk0 = static_cast<int>(static_cast<int64_t>(w) * nblk / kW);
   const int nb = static_cast<int>(static_cast<int64_t>(w + 1) * nblk / kW) - blk0;
 
@@ -324,9 +325,9 @@ __device__ __forceinline__ void decode_seq_body(
     const int64_t stride = static_cast<int64_t>(Hkv) * G::kTile;
     // a run that starts inside the sequence's shared prefix reads through the caches
     if (cached != nullptr && blk0 < cached[b])
-      stream_blocks<D, FP8, kU, kPipe, kTR, false>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+      stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
     else
-      stream_blocks<D, FP8, kU, kPipe, kTR, true>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+      stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
   }
   const float l = sum_rows<D, FP8>(sm);
 
@@ -358,13 +359,13 @@ __device__ __forceinline__ void decode_seq_body(
 }
 
 // One workgroup per (sequence, head); see decode_seq_body.
-template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR>
+template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
 __global__ __launch_bounds__(kW * 64) void decode_seq_kernel(
     const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cached, float* __restrict__ out, int32_t B, int32_t Hq, int32_t Hkv,
     int32_t max_blocks, int32_t ctx_cap, int32_t num_blocks, float qk_scale, float v_scale) {
-  decode_seq_body<D, FP8, kU, kPipe, kW, kTR>(blockIdx.x, q, kc, vc, tables, lens, cached, out, B, Hq,
+  decode_seq_body<D, FP8, kU, kPipe, kW, kTR, BS>(blockIdx.x, q, kc, vc, tables, lens, cached, out, B, Hq,
                                               Hkv, max_blocks, ctx_cap, num_blocks, qk_scale, v_scale);
 }
 

@@ -19,7 +19,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBlock = 16;  // tokens per KV block the kernels are built for
 
 // fp32 -> OCP e4m3 code, round to nearest even.  |x| <= 448 and x not NaN
 // (the caller clamps).  Normal range: round the 23-bit mantissa to 3 bits with

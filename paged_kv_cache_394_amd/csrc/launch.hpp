@@ -43,7 +43,8 @@ hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t to
 
 // Mixed step: chunked prefill of some sequences and decode of others in one
 // launch (fp16 caches).  The decode half supports contexts up to
-// mixed_max_context() tokens; the caller falls back to two launches beyond.
+// mixed_max_context(block_size) tokens; the caller falls back to two launches
+// beyond.
 struct MixedPrefill {
   const void* q;
   int32_t total_q;
@@ -57,7 +58,7 @@ struct MixedDecode {
   int32_t B, max_blocks, max_ctx;
   float* out;
 };
-int32_t mixed_max_context();
+int32_t mixed_max_context(int32_t block_size);
 hipError_t launch_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
                         const MixedDecode& d, hipStream_t s);
 

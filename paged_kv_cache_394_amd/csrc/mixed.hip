@@ -25,7 +25,7 @@ constexpr int kMixU = 2;
 constexpr int kMixW = 4;
 static_assert(kMixW * 64 == kThreads, "decode and prefill workgroups have one shape");
 
-template <int D, int kTR>
+template <int D, int kTR, int BS>
 __global__ __launch_bounds__(kThreads, 2) void mixed_step_kernel(
     const half_t* __restrict__ pq, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
@@ -37,17 +37,17 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_step_kernel(
     int32_t ctx_cap) {
   const int wg = blockIdx.x;
   if (wg < n_prefill_wgs) {
-    prefill_body<D>(wg, pq, kc, vc, cu_q, prior, ptables, pout, Bp, Hq, Hkv, total_q, pmax_blocks,
+    prefill_body<D, BS>(wg, pq, kc, vc, cu_q, prior, ptables, pout, Bp, Hq, Hkv, total_q, pmax_blocks,
                     num_blocks, nqt, qk_scale);
   } else {
-    decode_seq_body<D, false, kMixU, false, kMixW, kTR>(
+    decode_seq_body<D, false, kMixU, false, kMixW, kTR, BS>(
         wg - n_prefill_wgs, dq, reinterpret_cast<const uint8_t*>(kc),
         reinterpret_cast<const uint8_t*>(vc), dtables, lens, cached, dout, Bd, Hq, Hkv, dmax_blocks,
         ctx_cap, num_blocks, qk_scale, 1.0f);
   }
 }
 
-template <int D, int kTR>
+template <int D, int kTR, int BS>
 hipError_t run_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
                      const MixedDecode& d, hipStream_t s) {
   const int32_t nqt = (p.max_chunk + kBq - 1) / kBq;
@@ -55,8 +55,8 @@ hipError_t run_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefil
   const int64_t n_prefill = (pairs + kXcds - 1) / kXcds * kXcds * nqt;
   const int64_t n_decode = static_cast<int64_t>(d.B) * Hq;
   const int32_t ctx_cap =
-      static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * kBlock, d.max_ctx));
-  mixed_step_kernel<D, kTR><<<dim3(static_cast<uint32_t>(n_prefill + n_decode)), dim3(kThreads), 0, s>>>(
+      static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * BS, d.max_ctx));
+  mixed_step_kernel<D, kTR, BS><<<dim3(static_cast<uint32_t>(n_prefill + n_decode)), dim3(kThreads), 0, s>>>(
       static_cast<const half_t*>(p.q), static_cast<const half_t*>(c.k),
       static_cast<const half_t*>(c.v), p.cu_q, p.prior, p.tables, p.out, p.B, Hq, c.num_kv_heads,
       p.total_q, p.max_blocks, c.num_blocks, nqt, scale * kLog2e, static_cast<int32_t>(n_prefill),
@@ -64,24 +64,38 @@ hipError_t run_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefil
   return hipGetLastError();
 }
 
+template <int BS>
+hipError_t launch_mixed_bs(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
+                           const MixedDecode& d, hipStream_t s) {
+  // blocks per decode wave decide the block-id registers (64 per register)
+  const int64_t ctx = std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * BS, d.max_ctx);
+  const int64_t per_wave = ((ctx + BS - 1) / BS + kMixW - 1) / kMixW;
+  const int tr = per_wave <= 64 ? 1 : per_wave <= 128 ? 2 : 4;
+  if (c.head_dim == 128) {
+    if (tr == 1) return run_mixed<128, 1, BS>(c, Hq, scale, p, d, s);
+    if (tr == 2) return run_mixed<128, 2, BS>(c, Hq, scale, p, d, s);
+    return run_mixed<128, 4, BS>(c, Hq, scale, p, d, s);
+  }
+  if (tr == 1) return run_mixed<64, 1, BS>(c, Hq, scale, p, d, s);
+  if (tr == 2) return run_mixed<64, 2, BS>(c, Hq, scale, p, d, s);
+  return run_mixed<64, 4, BS>(c, Hq, scale, p, d, s);
+}
+
 }  // namespace
 
-int32_t mixed_max_context() { return 64 * 4 * kMixW * kBlock; }
+// A decode wave holds up to 4 block-id registers of 64 ids each.
+int32_t mixed_max_context(int32_t block_size) { return 64 * 4 * kMixW * block_size; }
 
 hipError_t launch_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
                         const MixedDecode& d, hipStream_t s) {
-  // blocks per decode wave decide the block-id registers (64 per register)
-  const int64_t ctx = std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * kBlock, d.max_ctx);
-  const int64_t per_wave = ((ctx + kBlock - 1) / kBlock + kMixW - 1) / kMixW;
-  const int tr = per_wave <= 64 ? 1 : per_wave <= 128 ? 2 : 4;
-  if (c.head_dim == 128) {
-    if (tr == 1) return run_mixed<128, 1>(c, Hq, scale, p, d, s);
-    if (tr == 2) return run_mixed<128, 2>(c, Hq, scale, p, d, s);
-    return run_mixed<128, 4>(c, Hq, scale, p, d, s);
+  switch (c.block_size) {
+    case 8:
+      return launch_mixed_bs<8>(c, Hq, scale, p, d, s);
+    case 32:
+      return launch_mixed_bs<32>(c, Hq, scale, p, d, s);
+    default:
+      return launch_mixed_bs<16>(c, Hq, scale, p, d, s);
   }
-  if (tr == 1) return run_mixed<64, 1>(c, Hq, scale, p, d, s);
-  if (tr == 2) return run_mixed<64, 2>(c, Hq, scale, p, d, s);
-  return run_mixed<64, 4>(c, Hq, scale, p, d, s);
 }
 
 }  // namespace pa

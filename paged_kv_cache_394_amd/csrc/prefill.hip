@@ -9,8 +9,8 @@
 // (v_mfma_f32_16x16x32_f16).
 //
 // Tiling.  A workgroup owns 128 query rows of one (sequence, head): 4 wave64s of
-// 32 rows (two 16-row sub-tiles).  Keys are walked in tiles of 64 (four 16-token
-// blocks looked up in the block table), staged through LDS: K row-major, V
+// 32 rows (two 16-row sub-tiles).  Keys are walked in tiles of 64 (8, 4 or 2
+// blocks of 8, 16 or 32 tokens looked up in the block table), staged through LDS: K row-major, V
 // transposed, so both MFMA operands are read as 16-byte LDS runs.
 // Each wave computes S^T = K Q^T (so a lane ends up holding the scores of one
 // query row, which makes the row max / sum and the output rescale lane-local up
@@ -50,27 +50,45 @@ namespace {
 using namespace dev;
 }  // namespace
 
-hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,
-                          const int32_t* cu_q, const int32_t* prior, const int32_t* tables,
-                          int32_t B, int32_t max_blocks, int32_t max_chunk, float scale, float* out,
-                          hipStream_t s) {
-  if (B <= 0 || max_chunk <= 0 || total_q <= 0) return hipSuccess;
+template <int BS>
+hipError_t launch_prefill_bs(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,
+                             const int32_t* cu_q, const int32_t* prior, const int32_t* tables,
+                             int32_t B, int32_t max_blocks, int32_t max_chunk, float scale,
+                             float* out, hipStream_t s) {
   const int32_t nqt = (max_chunk + kBq - 1) / kBq;
   const float qk_scale = scale * kLog2e;
   const int64_t pairs = static_cast<int64_t>(B) * Hq;
   const dim3 grid(static_cast<uint32_t>((pairs + kXcds - 1) / kXcds * kXcds * nqt));
   if (c.head_dim == 128) {
-    prefill_kernel<128><<<grid, dim3(kThreads), 0, s>>>(
+    prefill_kernel<128, BS><<<grid, dim3(kThreads), 0, s>>>(
         static_cast<const half_t*>(q), static_cast<const half_t*>(c.k),
         static_cast<const half_t*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
         max_blocks, c.num_blocks, nqt, qk_scale);
   } else {
-    prefill_kernel<64><<<grid, dim3(kThreads), 0, s>>>(
+    prefill_kernel<64, BS><<<grid, dim3(kThreads), 0, s>>>(
         static_cast<const half_t*>(q), static_cast<const half_t*>(c.k),
         static_cast<const half_t*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
         max_blocks, c.num_blocks, nqt, qk_scale);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,
+                          const int32_t* cu_q, const int32_t* prior, const int32_t* tables,
+                          int32_t B, int32_t max_blocks, int32_t max_chunk, float scale, float* out,
+                          hipStream_t s) {
+  if (B <= 0 || max_chunk <= 0 || total_q <= 0) return hipSuccess;
+  switch (c.block_size) {
+    case 8:
+      return launch_prefill_bs<8>(c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, max_chunk,
+                                  scale, out, s);
+    case 32:
+      return launch_prefill_bs<32>(c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, max_chunk,
+                                   scale, out, s);
+    default:
+      return launch_prefill_bs<16>(c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, max_chunk,
+                                   scale, out, s);
+  }
 }
 
 }  // namespace pa

@@ -65,19 +65,20 @@ __device__ __forceinline__ int work_rank(int Wb, int lane, int B) {
   return lane < B ? rank : 64;
 }
 
-// The 4 block ids of a key tile (wave-uniform scalar loads; ids past the
-// table's end, or outside the pool, read as block 0), as four scalars.
+// The block ids of a key tile (kBk / BS of them, at most 8; wave-uniform;
+// ids past the table's end, or outside the pool, read as block 0), as scalars.
 struct TileBlocks {
-  int p0, p1, p2, p3;
+  int p0, p1, p2, p3, p4, p5, p6, p7;
 };
 
-// Block j (0..3) of a tile.  A free function on values: as a member reading
+// Block j (0..7) of a tile.  A free function on values: as a member reading
 // this->pN the selects are folded into one indexed load and the struct is
 // left in memory.
-__device__ __forceinline__ int pick_block(int j, int p0, int p1, int p2, int p3) {
-  const int lo = (j & 1) ? p1 : p0;
-  const int hi = (j & 1) ? p3 : p2;
-  return (j & 2) ? hi : lo;
+__device__ __forceinline__ int pick_block(int j, const TileBlocks& t) {
+  const int a = (j & 1) ? t.p1 : t.p0, b = (j & 1) ? t.p3 : t.p2;
+  const int c = (j & 1) ? t.p5 : t.p4, d = (j & 1) ? t.p7 : t.p6;
+  const int lo = (j & 2) ? b : a, hi = (j & 2) ? d : c;
+  return (j & 4) ? hi : lo;
 }
 
 __device__ __forceinline__ int table_id(const int32_t* __restrict__ trow, int idx, int max_blocks,
@@ -87,85 +88,92 @@ __device__ __forceinline__ int table_id(const int32_t* __restrict__ trow, int id
   return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
 }
 
-// Lanes 0..3 load the 4 table entries of tile kt (a vector load, waited on
-// in order with the tile loads, one tile ahead of use).
+// Lanes 0 .. kBk/BS - 1 load the table entries of tile kt (a vector load,
+// waited on in order with the tile loads, one tile ahead of use).
+template <int BS>
 __device__ __forceinline__ int tile_ids_lanes(const int32_t* __restrict__ trow, int kt, int max_blocks,
                                               int lane) {
-  const int j = kt * (kBk / kBlock) + lane;
-  return (lane < 4 && j < max_blocks) ? trow[j] : 0;
+  const int j = kt * (kBk / BS) + lane;
+  return (lane < kBk / BS && j < max_blocks) ? trow[j] : 0;
 }
 
 __device__ __forceinline__ int clamp_id(int v, int num_blocks) {
   return (static_cast<uint32_t>(v) < static_cast<uint32_t>(num_blocks)) ? v : 0;
 }
 
+template <int BS>
 __device__ __forceinline__ TileBlocks tile_blocks_from(int ids, int num_blocks) {
-  return TileBlocks{clamp_id(__builtin_amdgcn_readlane(ids, 0), num_blocks),
-                    clamp_id(__builtin_amdgcn_readlane(ids, 1), num_blocks),
-                    clamp_id(__builtin_amdgcn_readlane(ids, 2), num_blocks),
-                    clamp_id(__builtin_amdgcn_readlane(ids, 3), num_blocks)};
+  constexpr int n = kBk / BS;
+  auto at = [&](int j) { return j < n ? clamp_id(__builtin_amdgcn_readlane(ids, j), num_blocks) : 0; };
+  return TileBlocks{at(0), at(1), at(2), at(3), at(4), at(5), at(6), at(7)};
 }
 
+template <int BS>
 __device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ trow, int kt,
                                                   int max_blocks, int num_blocks) {
-  const int j0 = kt * (kBk / kBlock);
-  return TileBlocks{table_id(trow, j0, max_blocks, num_blocks),
-                    table_id(trow, j0 + 1, max_blocks, num_blocks),
-                    table_id(trow, j0 + 2, max_blocks, num_blocks),
-                    table_id(trow, j0 + 3, max_blocks, num_blocks)};
+  constexpr int n = kBk / BS;
+  const int j0 = kt * n;
+  auto at = [&](int j) { return j < n ? table_id(trow, j0 + j, max_blocks, num_blocks) : 0; };
+  return TileBlocks{at(0), at(1), at(2), at(3), at(4), at(5), at(6), at(7)};
 }
 
-// Per-thread staging geometry.  K load i of thread t is 16-byte chunk
-// i * 256 + t of the tile: key (i * 256 + t) / CPR, which lies in block
-// (i * 256 + 64 w) / (16 CPR) of the tile for wave w (the same for the whole
-// wave) at the same in-block row and column for every i.  Thread t < VTHREADS
-// stages V granule q = t / (D/4) (pair p = q / 4, group g = q % 4) for
-// columns 4 dq .. 4 dq + 3, dq = t % (D/4): rows 4 g .. 4 g + 3 of blocks
-// 2 p and 2 p + 1 of the tile (one pair of blocks per wave).
-template <int D>
+// Per-thread staging geometry for BS-token blocks.  K load i of thread t is
+// 16-byte chunk i * 256 + t of the tile: key (i * 256 + t) / CPR; the 64 / CPR
+// keys a wave loads per instruction are consecutive and aligned, so they lie
+// in one block (wave-uniform base).  V: thread (w, lane < D/2) stages granule
+// q = 2 w + lane / (D/4) (pair p = q / 4, group g = q % 4) for columns
+// 4 dq .. 4 dq + 3, dq = lane % (D/4): keys 32 p + 16 hb + 4 g + i (hb < 2,
+// i < 4), rows of block (32 p + 16 hb + 4 g) / BS -- the same block for the
+// whole wave at each hb, for every block size 8, 16 and 32.
+template <int D, int BS>
 struct StageGeom {
-  int k_off;    // halfs from a block's (kv head) base to the thread's K chunk
   int k_row;    // the chunk's key within the tile, for i = 0 (adds 256 i / CPR)
   int k_col;    // its chunk index
+  int k_head;   // halfs from a block's base to this kv head's rows
   bool v_on;    // thread stages V
   int vq, dq;   // granule (0..7) and column quad
-  int v_off;    // halfs from a block's (kv head) base to row 4 g, column 4 dq
+  int v_off[2]; // halfs from a block's base to the thread's first V row, per hb
 
   __device__ void init(int tid, int kvh) {
     using G = PGeom<D>;
+    const int w = tid >> 6, lane = tid & 63;
     k_row = tid / G::CPR;
     k_col = tid % G::CPR;
-    k_off = (kvh * kBlock + (k_row & 15)) * D + k_col * 8;
-    v_on = tid < G::VTHREADS;
-    vq = (tid / (D / 4)) & 7;
-    dq = tid % (D / 4);
-    v_off = (kvh * kBlock + 4 * (vq & 3)) * D + 4 * dq;
+    k_head = kvh * BS * D;
+    v_on = lane < D / 2;
+    vq = (2 * w + lane / (D / 4)) & 7;
+    dq = lane % (D / 4);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+      v_off[hb] = (kvh * BS + (16 * hb + 4 * (vq & 3)) % BS) * D + 4 * dq;
   }
 };
 
 // Issue the global loads of a key tile.  Every load stays inside the pool;
 // rows past the context are fixed up by store_tile.
-template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D>& sg, const TileBlocks& tb,
+template <int D, int BS>
+__device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D, BS>& sg, const TileBlocks& tb,
                                           const half_t* __restrict__ kc,
                                           const half_t* __restrict__ vc, int64_t blk_stride,
                                           int w) {
   using G = PGeom<D>;
 #pragma unroll
   for (int i = 0; i < G::KLOADS; ++i) {
-    const int blk = (i * kThreads + 64 * w) / (kBlock * G::CPR);  // wave-uniform
-    const half_t* base = kc + static_cast<int64_t>(pick_block(blk, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
-    st.k[i] = *reinterpret_cast<const u32x4_t*>(base + sg.k_off);
+    const int key = sg.k_row + i * (kThreads / G::CPR);
+    const int blk = ((i * kThreads + 64 * w) / G::CPR) / BS;  // wave-uniform
+    const half_t* base = kc + static_cast<int64_t>(pick_block(blk, tb)) * blk_stride;
+    st.k[i] = *reinterpret_cast<const u32x4_t*>(base + sg.k_head + (key % BS) * D + sg.k_col * 8);
   }
   if (sg.v_on) {
-    // pair p = vq / 4 is wave-uniform: 64 threads cover 64 / (D/4) granules of one pair
-    const int p = __builtin_amdgcn_readfirstlane(sg.vq >> 2);
-    const half_t* b0 = vc + static_cast<int64_t>(pick_block(2 * p, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
-    const half_t* b1 = vc + static_cast<int64_t>(pick_block(2 * p + 1, tb.p0, tb.p1, tb.p2, tb.p3)) * blk_stride;
+    // pair p = w / 2 and group pair g / 2 = w % 2 are wave-uniform
+    const int kb = 32 * (w >> 1) + 8 * (w & 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = *reinterpret_cast<const u32x2_t*>(b0 + sg.v_off + i * D);
+    for (int hb = 0; hb < 2; ++hb) {
+      const half_t* base = vc + static_cast<int64_t>(pick_block((kb + 16 * hb) / BS, tb)) * blk_stride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[4 + i] = *reinterpret_cast<const u32x2_t*>(b1 + sg.v_off + i * D);
+      for (int i = 0; i < 4; ++i)
+        st.v[4 * hb + i] = *reinterpret_cast<const u32x2_t*>(base + sg.v_off[hb] + i * D);
+    }
   }
 }
 
@@ -173,8 +181,8 @@ __device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D>& sg, 
 // tile holding the end of the keys (tail), V rows at or past n_keys are zeroed
 // (their P is 0, but stale cache rows may hold non-finite bits); K rows there
 // only produce scores that the causal mask removes.
-template <int D>
-__device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D>& sg, half_t* __restrict__ sK,
+template <int D, int BS>
+__device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D, BS>& sg, half_t* __restrict__ sK,
                                            half_t* __restrict__ sVt, bool tail, int key0, int n_keys) {
   using G = PGeom<D>;
 #pragma unroll
@@ -203,7 +211,7 @@ __device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D>& sg,
 }
 
 // grid (ceil(B * Hq / 8) * 8 * nqt), block 256.  qk_scale = softmax scale * log2 e.
-template <int D>
+template <int D, int BS>
 __device__ __forceinline__ void prefill_body(
     int u, const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
@@ -242,7 +250,7 @@ __device__ __forceinline__ void prefill_body(
   const int P = max(prior[b], 0);
   const int q0 = qt * kBq;
   if (q0 >= C || row0 < 0) return;
-  const int L_total = min(P + C, max_blocks * kBlock);
+  const int L_total = min(P + C, max_blocks * BS);
   const int kvh = h / (Hq / Hkv);
   const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
 
@@ -284,24 +292,24 @@ __device__ __forceinline__ void prefill_body(
   const int n_keys = min(P + min(q0 + kBq, C), L_total);  // keys any row of the group needs
   const int ntiles = (n_keys + kBk - 1) / kBk;
 
-  StageGeom<D> sg;
+  StageGeom<D, BS> sg;
   sg.init(tid, kvh);
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * kBlock * D;
+  const int64_t blk_stride = static_cast<int64_t>(Hkv) * BS * D;
   Stage<D> stg;
   int ids_next = 0;
   if (ntiles > 0) {
-    load_tile<D>(stg, sg, tile_blocks(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
-    ids_next = tile_ids_lanes(trow, 1, max_blocks, lane);
-    store_tile<D>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
+    load_tile<D, BS>(stg, sg, tile_blocks<BS>(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
+    ids_next = tile_ids_lanes<BS>(trow, 1, max_blocks, lane);
+    store_tile<D, BS>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
   }
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int key0 = kt * kBk;
     const bool more = kt + 1 < ntiles;
     if (more) {
-      const TileBlocks tb = tile_blocks_from(ids_next, num_blocks);
-      ids_next = tile_ids_lanes(trow, kt + 2, max_blocks, lane);
-      load_tile<D>(stg, sg, tb, kc, vc, blk_stride, w);
+      const TileBlocks tb = tile_blocks_from<BS>(ids_next, num_blocks);
+      ids_next = tile_ids_lanes<BS>(trow, kt + 2, max_blocks, lane);
+      load_tile<D, BS>(stg, sg, tb, kc, vc, blk_stride, w);
     }
     __syncthreads();  // buffer kt % 2 written; buffer (kt + 1) % 2 no longer read
     const half_t* cK = sK + (kt & 1) * G::KBUF;
@@ -399,7 +407,7 @@ __device__ __forceinline__ void prefill_body(
       }
     }
     if (more)
-      store_tile<D>(stg, sg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF,
+      store_tile<D, BS>(stg, sg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF,
                     key0 + 2 * kBk > n_keys, key0 + kBk, n_keys);
   }
 
@@ -419,14 +427,14 @@ __device__ __forceinline__ void prefill_body(
 }
 
 
-template <int D>
+template <int D, int BS>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
     const int32_t* __restrict__ tables, float* __restrict__ out, int32_t B, int32_t Hq,
     int32_t Hkv, int32_t total_q, int32_t max_blocks, int32_t num_blocks, int32_t nqt,
     float qk_scale) {
-  prefill_body<D>(blockIdx.x, q, kc, vc, cu_q, prior, tables, out, B, Hq, Hkv, total_q, max_blocks,
+  prefill_body<D, BS>(blockIdx.x, q, kc, vc, cu_q, prior, tables, out, B, Hq, Hkv, total_q, max_blocks,
                   num_blocks, nqt, qk_scale);
 }
 

@@ -20,7 +20,8 @@ template <bool FP8>
 __global__ __launch_bounds__(256) void write_kv_kernel(
     const half_t* __restrict__ k_new, const half_t* __restrict__ v_new,
     const int32_t* __restrict__ slots, void* __restrict__ k_cache, void* __restrict__ v_cache,
-    int32_t T, int32_t Hkv, int32_t D, int64_t n_slots, float k_scale, float v_scale) {
+    int32_t T, int32_t Hkv, int32_t D, int32_t bs_log2, int64_t n_slots, float k_scale,
+    float v_scale) {
   const int32_t chunks = D >> 3;  // 8-value chunks per row
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(T) * Hkv * chunks;
@@ -31,9 +32,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   const int64_t t = row / Hkv;
   const int32_t slot = slots[t];
   if (slot < 0 || slot >= n_slots) return;  // padding or out of range: skipped
-  const int64_t blk = slot >> 4;
-  const int32_t off = slot & (kBlock - 1);
-  const int64_t dst = ((blk * Hkv + h) * kBlock + off) * D + static_cast<int64_t>(c) * 8;
+  const int64_t blk = slot >> bs_log2;
+  const int32_t off = slot & ((1 << bs_log2) - 1);
+  const int64_t dst = (((blk * Hkv + h) << bs_log2) + off) * D + static_cast<int64_t>(c) * 8;
   const int64_t src = row * D + static_cast<int64_t>(c) * 8;
   const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(k_new + src);
   const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(v_new + src);
@@ -85,22 +86,23 @@ hipError_t launch_write_kv(const KvDesc& c, const void* k_new, const void* v_new
   if (T <= 0) return hipSuccess;
   const int64_t total = static_cast<int64_t>(T) * c.num_kv_heads * (c.head_dim / 8);
   const int64_t grid = (total + 255) / 256;
-  const int64_t n_slots = static_cast<int64_t>(c.num_blocks) * kBlock;
+  const int64_t n_slots = static_cast<int64_t>(c.num_blocks) * c.block_size;
+  const int32_t lb = __builtin_ctz(static_cast<unsigned>(c.block_size));  // a power of two
   if (c.fp8) {
     write_kv_kernel<true><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
         static_cast<const half_t*>(k_new), static_cast<const half_t*>(v_new), slots, c.k, c.v, T,
-        c.num_kv_heads, c.head_dim, n_slots, c.k_scale, c.v_scale);
+        c.num_kv_heads, c.head_dim, lb, n_slots, c.k_scale, c.v_scale);
   } else {
     write_kv_kernel<false><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
         static_cast<const half_t*>(k_new), static_cast<const half_t*>(v_new), slots, c.k, c.v, T,
-        c.num_kv_heads, c.head_dim, n_slots, c.k_scale, c.v_scale);
+        c.num_kv_heads, c.head_dim, lb, n_slots, c.k_scale, c.v_scale);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_copy_blocks(const KvDesc& c, const int32_t* pairs, int32_t n, hipStream_t s) {
   const int64_t block_bytes =
-      static_cast<int64_t>(c.num_kv_heads) * kBlock * c.head_dim * (c.fp8 ? 1 : 2);
+      static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * (c.fp8 ? 1 : 2);
   for (int32_t first = 0; first < n; first += kMaxPairsPerLaunch) {
     const int32_t cnt = (n - first < kMaxPairsPerLaunch) ? (n - first) : kMaxPairsPerLaunch;
     CopyPairs p{};

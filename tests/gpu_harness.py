@@ -28,22 +28,36 @@ def close(got: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL):
     return float(err.max()) if err.size else 0.0
 
 
+def pool_geometry(w: workloads.Workload, block_size: int, extra_seqs: int = 0):
+    """(num_blocks, initial free order) for ``w``'s token capacity at
+    ``block_size``.  The workloads count their pools in 16-token blocks; other
+    block sizes get the same capacity in tokens, one spare block per sequence
+    for rounding, and a seeded shuffle of their own."""
+    if block_size == 16:
+        return w.num_blocks, w.init_free_order
+    nb = -(-w.num_blocks * 16 // block_size) + w.batch + extra_seqs + 8
+    order = np.random.default_rng(1000 + w.seed + block_size).permutation(nb).astype(np.int32)
+    return nb, order
+
+
 class DecodeCase:
     """Library-side state of one decode workload on the GPU."""
 
     def __init__(self, w: workloads.Workload, fp8: bool = False, seqs=None, device="cuda",
-                 poison: bool = True):
+                 poison: bool = True, block_size: int = 16):
         self.w = w
         self.fp8 = fp8
+        self.bs = block_size
         seqs = list(range(w.batch)) if seqs is None else list(seqs)
         self.seqs = seqs
         if fp8:
             self.k_scale, self.v_scale = fp8_scales(w, seqs)
         else:
             self.k_scale = self.v_scale = 1.0
-        self.pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
+        nb, order = pool_geometry(w, block_size)
+        self.pool = pa.pa_pool_create(nb, block_size, order)
         # stale rows of partly filled blocks hold NaN bit patterns unless written
-        self.cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim, fp8=fp8,
+        self.cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size, fp8=fp8,
                                 k_scale=self.k_scale, v_scale=self.v_scale, device=device,
                                 fill=(255 if fp8 else float("nan")) if poison else 0)
         self.ids = []
@@ -64,7 +78,7 @@ class DecodeCase:
         w = self.w
         lens = np.array([pa.pa_seq_table(self.pool, s)[1] for s in self.ids], dtype=np.int64)
         self.max_ctx = int(max(1, lens.max()))
-        self.max_blocks = max(1, -(-self.max_ctx // 16))
+        self.max_blocks = max(1, -(-self.max_ctx // self.bs))
         tables, lens32 = pa.pa_block_tables(self.pool, self.ids, self.max_blocks)
         self.tables_np = tables
         self.lens_np = lens32
@@ -114,3 +128,135 @@ def oracle_decode(w, pairs, seqs=None, fp8_scales_=None, scale=None):
         kh = h // (w.num_heads // w.num_kv_heads)
         out[(i, h)] = attention_fp64(w.q[b, h], k[:, kh], v[:, kh], w.scale if scale is None else scale)
     return out
+
+
+class PrefillCase:
+    """Library-side state of one chunked-prefill workload: prior context and
+    chunk written through the allocator, outputs poisoned with NaN."""
+
+    def __init__(self, w, block_size: int = 16):
+        self.w = w
+        self.bs = block_size
+        nb, order = pool_geometry(w, block_size)
+        self.pool = pa.pa_pool_create(nb, block_size, order)
+        self.cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size,
+                                fill=float("nan"))
+        self.ids = []
+        for b in range(w.batch):
+            s = pa.pa_seq_create(self.pool)
+            self.ids.append(s)
+            k, v = w.kv(b)
+            P, C = int(w.prior[b]), int(w.chunk[b])
+            for lo, n in ((0, P), (P, C)):      # prior context first, then the chunk
+                slots, _ = pa.pa_alloc_append(self.pool, s, n)
+                if n:
+                    pa.pa_write_kv(self.cache, torch.from_numpy(np.ascontiguousarray(k[lo:lo + n])).cuda(),
+                                   torch.from_numpy(np.ascontiguousarray(v[lo:lo + n])).cuda(),
+                                   torch.from_numpy(slots).cuda())
+        L = int(w.lens.max())
+        self.max_blocks = max(1, -(-L // block_size))
+        tables, _ = pa.pa_block_tables(self.pool, self.ids, self.max_blocks)
+        self.tables = torch.from_numpy(tables).cuda()
+        cu = np.concatenate([[0], np.cumsum(w.chunk)]).astype(np.int32)
+        self.cu_np = cu
+        self.cu = torch.from_numpy(cu).cuda()
+        self.prior = torch.from_numpy(w.prior.astype(np.int32)).cuda()
+        self.q = torch.from_numpy(w.q).cuda()
+        self.out = torch.full((int(cu[-1]), w.num_heads, w.head_dim), float("nan"),
+                              dtype=torch.float32, device="cuda")
+
+    def run(self, scale=None):
+        pa.pa_prefill_chunk(self.cache, self.q, self.cu, self.prior, self.tables,
+                            int(self.w.chunk.max()), self.w.scale if scale is None else scale, self.out)
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()
+
+    def ref_row(self, b, i, h, scale=None):
+        w = self.w
+        k, v = w.kv(b, cache=True)
+        kh = h // (w.num_heads // w.num_kv_heads)
+        n = int(w.prior[b]) + i + 1
+        r = int(self.cu_np[b]) + i
+        return attention_fp64(w.q[r, h], k[:n, kh], v[:n, kh], w.scale if scale is None else scale)
+
+
+class Mixed:
+    """One cache holding a prefill batch (prior context + chunk) and a decode
+    batch, with the argument dictionaries of pa_mixed_step for both halves."""
+
+    def __init__(self, wp, wd, block_size: int = 16):
+        assert (wp.num_heads, wp.num_kv_heads, wp.head_dim) == (wd.num_heads, wd.num_kv_heads, wd.head_dim)
+        self.wp, self.wd = wp, wd
+        n = pool_geometry(wp, block_size)[0] + pool_geometry(wd, block_size)[0]
+        self.pool = pa.pa_pool_create(n, block_size)
+        self.cache = pa.KvCache(n, wp.num_kv_heads, wp.head_dim, block_size=block_size,
+                                fill=float("nan"))
+        self.pids = []
+        for b in range(wp.batch):
+            s = pa.pa_seq_create(self.pool)
+            self.pids.append(s)
+            k, v = wp.kv(b)
+            P, C = int(wp.prior[b]), int(wp.chunk[b])
+            for lo, m in ((0, P), (P, C)):
+                slots, _ = pa.pa_alloc_append(self.pool, s, m)
+                if m:
+                    pa.pa_write_kv(self.cache, torch.from_numpy(np.ascontiguousarray(k[lo:lo + m])).cuda(),
+                                   torch.from_numpy(np.ascontiguousarray(v[lo:lo + m])).cuda(),
+                                   torch.from_numpy(slots).cuda())
+        self.dids = []
+        for b in range(wd.batch):
+            s = pa.pa_seq_create(self.pool)
+            self.dids.append(s)
+            k, v = wd.kv(b)
+            L = int(wd.lens[b])
+            slots, _ = pa.pa_alloc_append(self.pool, s, L)
+            if L:
+                pa.pa_write_kv(self.cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                               torch.from_numpy(slots).cuda())
+        H, D = wp.num_heads, wp.head_dim
+        pmax = max(1, -(-int(wp.lens.max()) // block_size))
+        tp, _ = pa.pa_block_tables(self.pool, self.pids, pmax)
+        cu = np.concatenate([[0], np.cumsum(wp.chunk)]).astype(np.int32)
+        self.cu_np = cu
+        self.prefill = dict(q=torch.from_numpy(wp.q).cuda(), cu_q=torch.from_numpy(cu).cuda(),
+                            prior=torch.from_numpy(wp.prior.astype(np.int32)).cuda(),
+                            tables=torch.from_numpy(tp).cuda(), max_chunk=int(wp.chunk.max()),
+                            out=torch.full((int(cu[-1]), H, D), float("nan"), device="cuda"))
+        self.max_ctx = max(1, int(wd.lens.max()))
+        dmax = max(1, -(-self.max_ctx // block_size))
+        td, lens = pa.pa_block_tables(self.pool, self.dids, dmax)
+        self.decode = dict(q=torch.from_numpy(wd.q).cuda(), tables=torch.from_numpy(td).cuda(),
+                           lens=torch.from_numpy(lens).cuda(), max_context_len=self.max_ctx,
+                           out=torch.full((wd.batch, H, D), float("nan"), device="cuda"),
+                           workspace=torch.empty(max(16, pa.pa_decode_workspace_bytes(
+                               wd.batch, H, D, self.max_ctx)), dtype=torch.uint8, device="cuda"))
+
+    def run_mixed(self, scale):
+        pa.pa_mixed_step(self.cache, scale, self.prefill, self.decode)
+        torch.cuda.synchronize()
+        return self.prefill["out"].cpu().numpy().copy(), self.decode["out"].cpu().numpy().copy()
+
+    def run_separate(self, scale):
+        p = self.prefill
+        pa.pa_prefill_chunk(self.cache, p["q"], p["cu_q"], p["prior"], p["tables"], p["max_chunk"],
+                            scale, p["out"])
+        d = self.decode
+        pa.pa_decode(self.cache, d["q"], d["tables"], d["lens"], d["max_context_len"], scale, d["out"],
+                     d["workspace"])
+        torch.cuda.synchronize()
+        return p["out"].cpu().numpy().copy(), d["out"].cpu().numpy().copy()
+
+    def check_oracle(self, outp, outd, rows_per_seq=None):
+        wp, wd = self.wp, self.wd
+        for b in range(wp.batch):
+            k, v = wp.kv(b, cache=True)
+            C = int(wp.chunk[b])
+            rows = range(C) if rows_per_seq is None else sorted({0, C - 1, C // 2} & set(range(C)))
+            for i in rows:
+                r = int(self.cu_np[b]) + i
+                n = int(wp.prior[b]) + i + 1
+                for h in range(wp.num_heads):
+                    kh = h // (wp.num_heads // wp.num_kv_heads)
+                    close(outp[r, h], attention_fp64(wp.q[r, h], k[:n, kh], v[:n, kh], wp.scale))
+        ref = oracle_decode(wd, [(i, h) for i in range(wd.batch) for h in range(wd.num_heads)])
+        close(outd, np.array([[ref[(i, h)] for h in range(wd.num_heads)] for i in range(wd.batch)]))

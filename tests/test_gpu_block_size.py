@@ -1,0 +1,125 @@
+"""Block sizes 8, 16 and 32 ([p1] "PagedAttention" and "Block Size": the
+block size is a tuning knob; smaller blocks waste fewer slots, larger ones
+give the kernel longer contiguous runs).  Decode (split and per-sequence
+paths, fp16 and e4m3), chunked prefill and the mixed step at each block size
+against the float64 oracle, and the same inputs giving the same answer at
+every block size up to the tolerance.  The KV write and copy-on-write at
+every block size are held bit-exact in the write test."""
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_harness import ATOL8, DecodeCase, Mixed, PrefillCase, close, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [8, 16, 32]
+
+
+def full_ref(case, fp8_ref=None):
+    w = case.w
+    pairs = [(i, h) for i in range(len(case.ids)) for h in range(w.num_heads)]
+    ref = oracle_decode(w, pairs, case.seqs, fp8_ref)
+    return np.stack([np.stack([ref[(i, h)] for h in range(w.num_heads)]) for i in range(len(case.ids))])
+
+
+@pytest.mark.parametrize("block_size", SIZES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_path_ragged(block_size, D):
+    """Lengths on both sides of every block boundary size and of the 512-token
+    partition; a narrow batch, so the split path with its merge runs."""
+    lens = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1100, 2049, 3000]
+    w = workloads.custom_decode(201 + D, lens, 8, 2, D)
+    case = DecodeCase(w, block_size=block_size)
+    assert case.tables_np.shape[1] == -(-3000 // block_size)
+    close(case.decode(), full_ref(case))
+
+
+@pytest.mark.parametrize("block_size", SIZES)
+def test_split_path_beyond_64_sequences(block_size):
+    """More than 64 sequences: the split units keep index order."""
+    rng = np.random.default_rng(211)
+    lens = rng.integers(0, 2500, size=72)
+    w = workloads.custom_decode(211, lens, 4, 2, 128)
+    case = DecodeCase(w, block_size=block_size)
+    got = case.decode()
+    assert np.all(got[lens == 0] == 0)
+    close(got, full_ref(case))
+
+
+@pytest.mark.parametrize("block_size", SIZES)
+@pytest.mark.parametrize("B,H,KVH,D,top", [(64, 32, 8, 128, 1500),   # 4 waves per workgroup
+                                           (30, 40, 40, 64, 700)])    # 8 waves per workgroup
+def test_per_sequence_path(block_size, B, H, KVH, D, top):
+    rng = np.random.default_rng(221 + B)
+    lens = rng.integers(1, top, size=B)
+    lens[3] = 0
+    lens[5] = top
+    w = workloads.custom_decode(221 + B, lens, H, KVH, D)
+    case = DecodeCase(w, block_size=block_size)
+    got = case.decode()
+    assert np.all(got[3] == 0)
+    close(got, full_ref(case))
+
+
+@pytest.mark.parametrize("block_size", SIZES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_decode(block_size, D):
+    lens = [1, 8, 33, 200, 513, 1100]
+    w = workloads.custom_decode(231 + D, lens, 4, 2, D)
+    if D * block_size < 1024:
+        import paged_kv_cache_394_amd as pa
+        with pytest.raises(pa.PaError) as e:
+            DecodeCase(w, fp8=True, block_size=block_size)
+        assert e.value.name == "unsupported"
+        return
+    case = DecodeCase(w, fp8=True, block_size=block_size)
+    got = case.decode()
+    # the kernel's own error: the fp16 bound against the dequantised cache
+    close(got, full_ref(case, (case.k_scale, case.v_scale)))
+    # the format's error against the fp16 source shrinks as a context averages
+    # more rows; with a handful of tokens one e4m3 rounding (2^-4 relative) of
+    # a few large values can pass 5e-2 on its own, so only the contexts of 200
+    # tokens and more are held to it
+    long_ = np.array(lens) >= 200
+    close(got[long_], full_ref(case)[long_], ATOL8, ATOL8)
+
+
+def test_same_answer_at_every_block_size():
+    """One batch through the three block sizes (different tables, run lengths
+    and split boundaries): results agree to the tolerance."""
+    lens = [3, 100, 640, 1999]
+    w = workloads.custom_decode(241, lens, 8, 8, 128)
+    outs = [DecodeCase(w, block_size=bs).decode().astype(np.float64) for bs in SIZES]
+    for o in outs[1:]:
+        close(o, outs[0])
+
+
+@pytest.mark.parametrize("block_size", SIZES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill(block_size, D):
+    """Ragged priors and chunks, one chunk of a single row, an empty prior."""
+    w = workloads.custom_prefill(251 + D, [0, 37, 300, 16, 0, 9], [1, 21, 200, 129, 64, 70], 4, 2, D)
+    case = PrefillCase(w, block_size=block_size)
+    got = case.run()
+    for b in range(w.batch):
+        for i in range(int(w.chunk[b])):
+            r = int(case.cu_np[b]) + i
+            for h in range(w.num_heads):
+                close(got[r, h], case.ref_row(b, i, h))
+
+
+@pytest.mark.parametrize("block_size", SIZES)
+@pytest.mark.parametrize("dlens", [[1, 0, 37, 300, 1600], [10000, 700]])
+def test_mixed_step(block_size, dlens):
+    """One-launch mixed step (and, at block size 8 with a 10000-token context,
+    past its one-launch limit, the two-launch fallback)."""
+    wp = workloads.custom_prefill(261, [0, 37, 300], [1, 130, 200], 4, 2, 128)
+    wd = workloads.custom_decode(262, dlens, 4, 2, 128)
+    m = Mixed(wp, wd, block_size=block_size)
+    outp, outd = m.run_mixed(wp.scale)
+    sp, sd = m.run_separate(wp.scale)
+    assert np.array_equal(outp, sp)
+    close(outd, sd.astype(np.float64))
+    m.check_oracle(outp, outd)

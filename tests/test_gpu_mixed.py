@@ -11,88 +11,9 @@ import torch
 
 import paged_kv_cache_394_amd as pa
 import workloads
-from gpu_harness import close, oracle_decode
-from oracle import attention_fp64
+from gpu_harness import Mixed, close
 
 pytestmark = pytest.mark.gpu
-
-
-class Mixed:
-    def __init__(self, wp, wd, fp8=False):
-        assert (wp.num_heads, wp.num_kv_heads, wp.head_dim) == (wd.num_heads, wd.num_kv_heads, wd.head_dim)
-        self.wp, self.wd = wp, wd
-        n = wp.num_blocks + wd.num_blocks
-        self.pool = pa.pa_pool_create(n, 16)
-        self.cache = pa.KvCache(n, wp.num_kv_heads, wp.head_dim, fill=float("nan"))
-        self.pids = []
-        for b in range(wp.batch):
-            s = pa.pa_seq_create(self.pool)
-            self.pids.append(s)
-            k, v = wp.kv(b)
-            P, C = int(wp.prior[b]), int(wp.chunk[b])
-            for lo, m in ((0, P), (P, C)):
-                slots, _ = pa.pa_alloc_append(self.pool, s, m)
-                if m:
-                    pa.pa_write_kv(self.cache, torch.from_numpy(np.ascontiguousarray(k[lo:lo + m])).cuda(),
-                                   torch.from_numpy(np.ascontiguousarray(v[lo:lo + m])).cuda(),
-                                   torch.from_numpy(slots).cuda())
-        self.dids = []
-        for b in range(wd.batch):
-            s = pa.pa_seq_create(self.pool)
-            self.dids.append(s)
-            k, v = wd.kv(b)
-            L = int(wd.lens[b])
-            slots, _ = pa.pa_alloc_append(self.pool, s, L)
-            if L:
-                pa.pa_write_kv(self.cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
-                               torch.from_numpy(slots).cuda())
-        H, D = wp.num_heads, wp.head_dim
-        pmax = max(1, -(-int(wp.lens.max()) // 16))
-        tp, _ = pa.pa_block_tables(self.pool, self.pids, pmax)
-        cu = np.concatenate([[0], np.cumsum(wp.chunk)]).astype(np.int32)
-        self.cu_np = cu
-        self.prefill = dict(q=torch.from_numpy(wp.q).cuda(), cu_q=torch.from_numpy(cu).cuda(),
-                            prior=torch.from_numpy(wp.prior.astype(np.int32)).cuda(),
-                            tables=torch.from_numpy(tp).cuda(), max_chunk=int(wp.chunk.max()),
-                            out=torch.full((int(cu[-1]), H, D), float("nan"), device="cuda"))
-        self.max_ctx = max(1, int(wd.lens.max()))
-        dmax = max(1, -(-self.max_ctx // 16))
-        td, lens = pa.pa_block_tables(self.pool, self.dids, dmax)
-        self.decode = dict(q=torch.from_numpy(wd.q).cuda(), tables=torch.from_numpy(td).cuda(),
-                           lens=torch.from_numpy(lens).cuda(), max_context_len=self.max_ctx,
-                           out=torch.full((wd.batch, H, D), float("nan"), device="cuda"),
-                           workspace=torch.empty(max(16, pa.pa_decode_workspace_bytes(
-                               wd.batch, H, D, self.max_ctx)), dtype=torch.uint8, device="cuda"))
-
-    def run_mixed(self, scale):
-        pa.pa_mixed_step(self.cache, scale, self.prefill, self.decode)
-        torch.cuda.synchronize()
-        return self.prefill["out"].cpu().numpy().copy(), self.decode["out"].cpu().numpy().copy()
-
-    def run_separate(self, scale):
-        p = self.prefill
-        pa.pa_prefill_chunk(self.cache, p["q"], p["cu_q"], p["prior"], p["tables"], p["max_chunk"],
-                            scale, p["out"])
-        d = self.decode
-        pa.pa_decode(self.cache, d["q"], d["tables"], d["lens"], d["max_context_len"], scale, d["out"],
-                     d["workspace"])
-        torch.cuda.synchronize()
-        return p["out"].cpu().numpy().copy(), d["out"].cpu().numpy().copy()
-
-    def check_oracle(self, outp, outd, rows_per_seq=None):
-        wp, wd = self.wp, self.wd
-        for b in range(wp.batch):
-            k, v = wp.kv(b, cache=True)
-            C = int(wp.chunk[b])
-            rows = range(C) if rows_per_seq is None else sorted({0, C - 1, C // 2} & set(range(C)))
-            for i in rows:
-                r = int(self.cu_np[b]) + i
-                n = int(wp.prior[b]) + i + 1
-                for h in range(wp.num_heads):
-                    kh = h // (wp.num_heads // wp.num_kv_heads)
-                    close(outp[r, h], attention_fp64(wp.q[r, h], k[:n, kh], v[:n, kh], wp.scale))
-        ref = oracle_decode(wd, [(i, h) for i in range(wd.batch) for h in range(wd.num_heads)])
-        close(outd, np.array([[ref[(i, h)] for h in range(wd.num_heads)] for i in range(wd.batch)]))
 
 
 @pytest.mark.parametrize("dlens", [[1, 0, 37, 300, 1600],          # one block-id register per wave

@@ -8,54 +8,9 @@ import torch
 
 import paged_kv_cache_394_amd as pa
 import workloads
-from gpu_harness import close
-from oracle import attention_fp64
+from gpu_harness import PrefillCase, close
 
 pytestmark = pytest.mark.gpu
-
-
-class PrefillCase:
-    def __init__(self, w):
-        self.w = w
-        self.pool = pa.pa_pool_create(w.num_blocks, 16, w.init_free_order)
-        self.cache = pa.KvCache(w.num_blocks, w.num_kv_heads, w.head_dim, fill=float("nan"))
-        self.ids = []
-        for b in range(w.batch):
-            s = pa.pa_seq_create(self.pool)
-            self.ids.append(s)
-            k, v = w.kv(b)
-            P, C = int(w.prior[b]), int(w.chunk[b])
-            for lo, n in ((0, P), (P, C)):      # prior context first, then the chunk
-                slots, _ = pa.pa_alloc_append(self.pool, s, n)
-                if n:
-                    pa.pa_write_kv(self.cache, torch.from_numpy(np.ascontiguousarray(k[lo:lo + n])).cuda(),
-                                   torch.from_numpy(np.ascontiguousarray(v[lo:lo + n])).cuda(),
-                                   torch.from_numpy(slots).cuda())
-        L = int(w.lens.max())
-        self.max_blocks = max(1, -(-L // 16))
-        tables, _ = pa.pa_block_tables(self.pool, self.ids, self.max_blocks)
-        self.tables = torch.from_numpy(tables).cuda()
-        cu = np.concatenate([[0], np.cumsum(w.chunk)]).astype(np.int32)
-        self.cu_np = cu
-        self.cu = torch.from_numpy(cu).cuda()
-        self.prior = torch.from_numpy(w.prior.astype(np.int32)).cuda()
-        self.q = torch.from_numpy(w.q).cuda()
-        self.out = torch.full((int(cu[-1]), w.num_heads, w.head_dim), float("nan"),
-                              dtype=torch.float32, device="cuda")
-
-    def run(self, scale=None):
-        pa.pa_prefill_chunk(self.cache, self.q, self.cu, self.prior, self.tables,
-                            int(self.w.chunk.max()), self.w.scale if scale is None else scale, self.out)
-        torch.cuda.synchronize()
-        return self.out.cpu().numpy()
-
-    def ref_row(self, b, i, h, scale=None):
-        w = self.w
-        k, v = w.kv(b, cache=True)
-        kh = h // (w.num_heads // w.num_kv_heads)
-        n = int(w.prior[b]) + i + 1
-        r = int(self.cu_np[b]) + i
-        return attention_fp64(w.q[r, h], k[:n, kh], v[:n, kh], w.scale if scale is None else scale)
 
 
 def check_all(case, scale=None):

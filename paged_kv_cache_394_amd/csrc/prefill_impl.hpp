@@ -3,6 +3,7 @@
 // The design notes are at the top of prefill.hip.
 #pragma once
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -40,6 +41,11 @@ struct PGeom {
 };
 
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 2)) & 7; }
+
+constexpr half2_t kOnes2 = {static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
+
+__device__ __forceinline__ float maxf(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max4(float4_t v) { return maxf(maxf(v[0], v[1]), maxf(v[2], v[3])); }
 
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
@@ -303,7 +309,29 @@ __device__ __forceinline__ void prefill_body(
     store_tile<D, BS>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
   }
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // Per-lane byte offsets of the MFMA operand reads.  The K swizzle of row
+  // 16 ks + c16 depends on ks only through its parity, and the V^T swizzle of
+  // row 16 dt + c16 on dt only through its parity, so four registers each
+  // cover every read; the rest of each address is an immediate.
+  int k_rd[G::DK][2], v_rd[2][2];
+#pragma unroll
+  for (int kk = 0; kk < G::DK; ++kk)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      k_rd[kk][par] = 2 * (c16 * D + (((4 * kk + g) ^ kswz<D>(16 * par + c16)) << 3));
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      v_rd[kp][par] = 2 * (c16 * kBk + (((4 * kp + g) ^ swz8(16 * par + c16)) << 3));
+  const char* sKb = reinterpret_cast<const char*>(sK);
+  const char* sVb = reinterpret_cast<const char*>(sVt);
+
+  // One key tile.  PAR (the LDS buffer holding tile kt) is a compile-time
+  // constant: the loop below runs tiles in pairs, so every LDS address is a
+  // per-lane register plus an immediate offset.
+  auto step = [&](auto par, int kt) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
     const int key0 = kt * kBk;
     const bool more = kt + 1 < ntiles;
     if (more) {
@@ -311,9 +339,7 @@ __device__ __forceinline__ void prefill_body(
       ids_next = tile_ids_lanes<BS>(trow, kt + 2, max_blocks, lane);
       load_tile<D, BS>(stg, sg, tb, kc, vc, blk_stride, w);
     }
-    __syncthreads();  // buffer kt % 2 written; buffer (kt + 1) % 2 no longer read
-    const half_t* cK = sK + (kt & 1) * G::KBUF;
-    const half_t* cVt = sVt + (kt & 1) * G::VBUF;
+    __syncthreads();  // buffer PAR written; buffer 1 - PAR no longer read
 
     if (!(wq_last < wq_first || key0 > P + wq_last)) {  // keys of this tile visible to the wave
       // S^T tiles: [st][ks] holds keys key0 + 16 ks + 4 g + i for query row c16
@@ -327,8 +353,8 @@ __device__ __forceinline__ void prefill_body(
         half8_t a[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          a[ks] = *reinterpret_cast<const half8_t*>(
-              &cK[(ks * 16 + c16) * D + (((4 * kk + g) ^ kswz<D>(ks * 16 + c16)) << 3)]);
+          a[ks] = *reinterpret_cast<const half8_t*>(sKb + 2 * (PAR * G::KBUF + ks * 16 * D) +
+                                                    k_rd[kk][ks & 1]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -348,23 +374,24 @@ __device__ __forceinline__ void prefill_body(
         }
       }
 
-      half_t ph[2][4][4];
+      // P in fp16, two keys a register: pk[st][ks][j] = keys 4 g + 2 j, + 1 of sub-tile ks
+      half2_t pk[2][4][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float mt = -INFINITY;
+        // NaN-propagating maximum: gfx950 forms it into three-input max
+        // instructions without the quieting step the IEEE maxNum needs
+        float mt = max4(sacc[st][0]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          mt = fmaxf(mt, fmaxf(fmaxf(sacc[st][ks][0], sacc[st][ks][1]),
-                               fmaxf(sacc[st][ks][2], sacc[st][ks][3])));
+        for (int ks = 1; ks < 4; ++ks) mt = maxf(mt, max4(sacc[st][ks]));
         // move the running max (and rescale) only when some lane's scores grew
         // past it by more than 2^kLazyRescale: exp2 arguments stay <=
         // kLazyRescale.  The lane-local max decides; the row max over the 4
         // lane groups is only formed when a rescale happens.
         const float grow = (mt - m[st]) * c;  // +inf on the first visible tile
         if (__ballot(grow > kLazyRescale) != 0) {
-          mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-          const float m_new = fmaxf(m[st], mt);
+          mt = maxf(mt, __shfl_xor(mt, 16, 64));
+          mt = maxf(mt, __shfl_xor(mt, 32, 64));
+          const float m_new = maxf(m[st], mt);
           const float corr = (m[st] == -INFINITY) ? 0.f : fast_exp2((m[st] - m_new) * c);
           l[st] *= corr;
 #pragma unroll
@@ -372,14 +399,17 @@ __device__ __forceinline__ void prefill_body(
           m[st] = m_new;
         }
         const float mc = (m[st] == -INFINITY) ? 0.f : m[st] * c;
+        // the row sum adds the fp16 values the P.V product uses (exact
+        // products, fp32 accumulation): one dot2 per two keys
         float ps = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pr = fast_exp2(fmaf(sacc[st][ks][i], c, -mc));
-            ps += pr;
-            ph[st][ks][i] = static_cast<half_t>(pr);
+          for (int j = 0; j < 2; ++j) {
+            const float p0 = fast_exp2(fmaf(sacc[st][ks][2 * j], c, -mc));
+            const float p1 = fast_exp2(fmaf(sacc[st][ks][2 * j + 1], c, -mc));
+            pk[st][ks][j] = half2_t{static_cast<half_t>(p0), static_cast<half_t>(p1)};
+            ps = __builtin_amdgcn_fdot2(pk[st][ks][j], kOnes2, ps, false);
           }
         }
         l[st] += ps;
@@ -391,15 +421,14 @@ __device__ __forceinline__ void prefill_body(
         half8_t bp[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          bp[st] = half8_t{ph[st][2 * kp][0], ph[st][2 * kp][1], ph[st][2 * kp][2], ph[st][2 * kp][3],
-                           ph[st][2 * kp + 1][0], ph[st][2 * kp + 1][1], ph[st][2 * kp + 1][2],
-                           ph[st][2 * kp + 1][3]};
+          const half2_t* a0 = pk[st][2 * kp];
+          const half2_t* a1 = pk[st][2 * kp + 1];
+          bp[st] = half8_t{a0[0][0], a0[0][1], a0[1][0], a0[1][1], a1[0][0], a1[0][1], a1[1][0], a1[1][1]};
         }
 #pragma unroll
         for (int dt = 0; dt < G::DT; ++dt) {
-          const int vr = dt * 16 + c16;
-          const half8_t a =
-              *reinterpret_cast<const half8_t*>(&cVt[vr * kBk + (((kp * 4 + g) ^ swz8(vr)) << 3)]);
+          const half8_t a = *reinterpret_cast<const half8_t*>(sVb + 2 * (PAR * G::VBUF + dt * 16 * kBk) +
+                                                              v_rd[kp][dt & 1]);
 #pragma unroll
           for (int st = 0; st < 2; ++st)
             o[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[st], o[st][dt], 0, 0, 0);
@@ -407,8 +436,13 @@ __device__ __forceinline__ void prefill_body(
       }
     }
     if (more)
-      store_tile<D, BS>(stg, sg, sK + ((kt + 1) & 1) * G::KBUF, sVt + ((kt + 1) & 1) * G::VBUF,
-                    key0 + 2 * kBk > n_keys, key0 + kBk, n_keys);
+      store_tile<D, BS>(stg, sg, sK + (1 - PAR) * G::KBUF, sVt + (1 - PAR) * G::VBUF,
+                        key0 + 2 * kBk > n_keys, key0 + kBk, n_keys);
+  };
+
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < ntiles) step(std::integral_constant<int, 1>{}, kt + 1);
   }
 
 #pragma unroll

@@ -459,11 +459,11 @@ def bench_prefill(pa, torch, np, workloads, reps, block_size=16):
 
 
 def bench_block_sizes(pa, torch, np, workloads, w, steps, warmup, at16):
-    """The 13B decode batch and the chunked-prefill batch at block sizes 8 and
-    32 (16 is the headline line): pa_decode bandwidth, the slots lost to
+    """The 13B decode batch and the chunked-prefill batch at block sizes 8, 32
+    and 64 (16 is the headline line): pa_decode bandwidth, the slots lost to
     partly filled last blocks, and prefill time."""
     res = {}
-    for bs in (8, 16, 32):
+    for bs in (8, 16, 32, 64):
         if bs == 16:
             d_ms, p_ms = at16
         else:
@@ -699,7 +699,7 @@ def main():
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
         torch.cuda.empty_cache()
-        log("block sizes 8 / 32")
+        log("block sizes 8 / 32 / 64")
         res["block_sizes"] = bench_block_sizes(pa, torch, np, workloads, w, args.steps, args.warmup,
                                                (dec_ms, res["prefill"]["ms"]))
     if not args.no_cpu_baseline:

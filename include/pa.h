@@ -40,7 +40,7 @@
  *   configure vLLM to use this well?": smaller blocks waste fewer slots at the tail
  *   of each sequence, larger ones mean shorter tables and longer contiguous reads).
  *   The host pool takes any block_size >= 1; the device kernels are compiled for
- *   block_size 8, 16 and 32, and an e4m3 tile must be at least 1 KiB
+ *   block_size 8, 16, 32 and 64, and an e4m3 tile must be at least 1 KiB
  *   (block_size * head_dim >= 1024: block_size 8 with e4m3 needs head_dim 128).
  */
 #ifndef PA_H
@@ -72,7 +72,7 @@ typedef struct {
   void *k_cache;          /* [num_blocks][num_kv_heads][block_size][head_dim]        */
   void *v_cache;          /* same shape as k_cache                                   */
   int32_t num_blocks;
-  int32_t block_size;     /* tokens per block: 8, 16 or 32 for the device calls      */
+  int32_t block_size;     /* tokens per block: 8, 16, 32 or 64 for the device calls  */
   int32_t num_kv_heads;
   int32_t head_dim;       /* 64 or 128                                               */
   int32_t dtype;          /* PA_KV_F16 or PA_KV_FP8_E4M3                             */
@@ -327,7 +327,7 @@ pa_status pa_swap_blocks(const pa_kv_cache *cache, void *host_k, void *host_v,
  * least pa_decode_workspace_bytes(...) (used only by batches too narrow to fill
  * the GPU with one workgroup per (sequence, head)).
  * Errors: BAD_ARG (shape, null pointers, num_heads % num_kv_heads, workspace too
- * small), UNSUPPORTED (block_size not 8/16/32, head_dim not 64/128, an e4m3 tile
+ * small), UNSUPPORTED (block_size not 8/16/32/64, head_dim not 64/128, an e4m3 tile
  * under 1 KiB), HIP. */
 pa_status pa_decode(const pa_kv_cache *cache, const void *q, int32_t num_heads,
                     const int32_t *tables_dev, const int32_t *lens_dev,
@@ -345,7 +345,7 @@ pa_status pa_decode(const pa_kv_cache *cache, const void *q, int32_t num_heads,
  * non-decreasing, cu_q[0] = 0.  prior_dev: device int32[B].  tables_dev: device
  * int32[B][max_blocks].  max_chunk: upper bound on cu_q[b+1] - cu_q[b].  out_dev:
  * device fp32 [total_q_rows][num_heads][head_dim].
- * Errors: BAD_ARG, UNSUPPORTED (block_size not 8/16/32, head_dim not 64/128, e4m3
+ * Errors: BAD_ARG, UNSUPPORTED (block_size not 8/16/32/64, head_dim not 64/128, e4m3
  * cache), HIP. */
 pa_status pa_prefill_chunk(const pa_kv_cache *cache, const void *q, int32_t num_heads,
                            int32_t total_q_rows, const int32_t *cu_q_dev, const int32_t *prior_dev,

@@ -26,8 +26,8 @@ pa_status check_cache(const pa_kv_cache* c, const char* fn, pa::KvDesc* d) {
     return fail(PA_ERR_BAD_ARG, f + ": caches must be 16-byte aligned");
   if (c->num_blocks < 1 || c->num_kv_heads < 1)
     return fail(PA_ERR_BAD_ARG, f + ": num_blocks and num_kv_heads must be >= 1");
-  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, f + ": kernels are built for block_size 8, 16 and 32");
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, f + ": kernels are built for block_size 8, 16, 32 and 64");
   if (static_cast<int64_t>(c->num_blocks) * c->block_size >= (int64_t(1) << 31))
     return fail(PA_ERR_BAD_ARG, f + ": num_blocks * block_size must be < 2^31");
   if (c->head_dim != 64 && c->head_dim != 128)

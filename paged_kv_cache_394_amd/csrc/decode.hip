@@ -1,6 +1,6 @@
 // Paged decode attention for gfx950: one query per (sequence, head) over a KV
-// cache scattered across physical blocks of 8, 16 or 32 tokens found through a
-// block table
+// cache scattered across physical blocks of 8, 16, 32 or 64 tokens found
+// through a block table
 // ([p1] "vLLM PagedAttention Deep Dive", section "PagedAttention Mechanism":
 // look up the physical blocks, gather their K/V, run standard attention).
 //
@@ -15,8 +15,9 @@
 //   block id is then taken with a lane read into a scalar register, so no
 //   dependent memory access sits inside the block loop.
 // * Coalesced tiles.  One (block, head) tile is block_size x head_dim contiguous
-//   values (at least 1 KiB: fp16, or e4m3 with block_size * head_dim >= 1024).
-//   Load instruction i of a wave reads bytes [1024 i, 1024 i + 1024) of the tile,
+//   values, streamed in units of up to 16 token rows (a 32- or 64-token tile
+//   is 2 or 4 contiguous units of the same block), each at least 1 KiB.
+//   Load instruction i of a wave reads bytes [1024 i, 1024 i + 1024) of a unit,
 //   16 bytes per lane, so each load is one fully used 1 KiB run.  A lane then
 //   holds 16 bytes of one token row; the lanes of one row (head_dim*bytes/16 of
 //   them) sit in one DPP row group, where the q.k partial sums are reduced with
@@ -68,15 +69,15 @@ struct UnitPos {
 // then the one partly filled split of each sequence sorted by size, largest
 // first (ties by sequence index), and last a zero-size unit for each empty
 // context, which writes its zero output.
-template <int kSplit, int BS>
+template <int kSplit, int kUnit>
 __device__ __forceinline__ UnitPos longest_first_unit(int f, const int32_t* __restrict__ lens,
                                                       int B, int ctx_cap, int lane) {
   int Lb = 0;
   if (lane < B) Lb = min(max(lens[lane], 0), ctx_cap);
-  const int nblk = (Lb + BS - 1) / BS;
-  const int F = nblk / kSplit;      // full splits
-  const int psz = nblk % kSplit;    // blocks in the partly filled split (0: none)
-  const bool has_tail = lane < B && (psz != 0 || nblk == 0);
+  const int nunit = (Lb + kUnit - 1) / kUnit;
+  const int F = nunit / kSplit;     // full splits
+  const int psz = nunit % kSplit;   // units in the partly filled split (0: none)
+  const bool has_tail = lane < B && (psz != 0 || nunit == 0);
   int pre = F;  // inclusive prefix sum of F over the lanes
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -129,13 +130,15 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
     float v_scale) {
   using G = Geom<D, FP8, BS>;
   static_assert(kSplit % kU == 0, "a split is a whole number of steps");
-  constexpr int kTR = (kSplit + 63) / 64;  // block-id registers per lane
+  static_assert(kSplit % G::kSub == 0, "a split is a whole number of blocks");
+  constexpr int kSplitBlocks = kSplit / G::kSub;
+  constexpr int kTR = (kSplitBlocks + 63) / 64;  // block-id registers per lane
   const int lane = threadIdx.x & 63;
   const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * kWPG + (threadIdx.x >> 6));
   const int h = unit % Hq;
   int b, split, L;
   if constexpr (kLongestFirst) {
-    const UnitPos pos = longest_first_unit<kSplit, BS>(unit / Hq, lens, B, ctx_cap, lane);
+    const UnitPos pos = longest_first_unit<kSplit, G::kUnit>(unit / Hq, lens, B, ctx_cap, lane);
     if (!pos.valid) return;
     b = pos.b;
     split = pos.split;
@@ -148,7 +151,8 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
     L = lens[b];
   }
   const int64_t bh = static_cast<int64_t>(b) * Hq + h;
-  const int blk0 = split * kSplit;
+  const int u0 = split * kSplit;         // first unit of the split
+  const int b0 = split * kSplitBlocks;   // and its block
   const int kvh = h / (Hq / Hkv);
   const int col = lane % G::kLpr;
   const int row = lane / G::kLpr;
@@ -156,30 +160,30 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
   // The split's block ids (entries past the table's end are not read) and q
   // are loaded together, before either is used.
   int tb[kTR];
-  load_block_ids<kTR>(tb, tables + static_cast<int64_t>(b) * max_blocks, blk0,
-                      min(kSplit, max_blocks - blk0), lane);
+  load_block_ids<kTR>(tb, tables + static_cast<int64_t>(b) * max_blocks, b0,
+                      min(kSplitBlocks, max_blocks - b0), lane);
   QReg<FP8> qr;
   qr.load(q + bh * D + col * G::kEpl);
 
   L = min(max(L, 0), ctx_cap);
-  const int nblk = (L + BS - 1) / BS;
-  if (blk0 >= nblk) {
+  const int nunit = (L + G::kUnit - 1) / G::kUnit;
+  if (u0 >= nunit) {
     if (split == 0) {  // empty context: zero output
       for (int d = lane; d < D; d += 64) out[bh * D + d] = 0.f;
     }
     return;
   }
-  const int nb = min(kSplit, nblk - blk0);
-  const int nsplit_b = (nblk + kSplit - 1) / kSplit;
+  const int nb = min(kSplit, nunit - u0);
+  const int nsplit_b = (nunit + kSplit - 1) / kSplit;
   clamp_block_ids<kTR>(tb, num_blocks);
   Softmax<D, FP8> sm;
   const uint8_t* kb = kc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
   const uint8_t* vb = vc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
   const int64_t stride = static_cast<int64_t>(Hkv) * G::kTile;
-  if (cached != nullptr && blk0 < cached[b])
-    stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+  if (cached != nullptr && b0 < cached[b])
+    stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
   else
-    stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+    stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
   const float l = sum_rows<D, FP8>(sm);
   if (row != 0) return;
   float* dst;
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ out, int6
   if (i < n) out[i] = 0.f;
 }
 
-int64_t ctx_blocks_of(int32_t max_ctx, int bs) { return (static_cast<int64_t>(max_ctx) + bs - 1) / bs; }
+int64_t ctx_units_of(int32_t max_ctx, int unit) { return (static_cast<int64_t>(max_ctx) + unit - 1) / unit; }
 
 int32_t ctx_cap_of(int32_t max_blocks, int32_t max_ctx, int bs) {
   return static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(max_blocks) * bs, max_ctx));
@@ -285,8 +289,8 @@ template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLonge
 hipError_t run_split(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                      const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
                      int32_t max_ctx, float scale, float* out, void* workspace, hipStream_t s) {
-  static_assert(kSplit * BS == kSplitTokens, "a split is kSplitTokens tokens");
-  const int64_t nsplit64 = (ctx_blocks_of(max_ctx, BS) + kSplit - 1) / kSplit;
+  static_assert(kSplit * Geom<D, FP8, BS>::kUnit == kSplitTokens, "a split is kSplitTokens tokens");
+  const int64_t nsplit64 = (ctx_units_of(max_ctx, Geom<D, FP8, BS>::kUnit) + kSplit - 1) / kSplit;
   const int32_t nsplit = static_cast<int32_t>(nsplit64);
   const int64_t units = nsplit64 * B * Hq;
   const int32_t ctx_cap = ctx_cap_of(max_blocks, max_ctx, BS);
@@ -344,19 +348,19 @@ constexpr int kSeqTR = 1;
 constexpr int64_t kSeqMinWaves = 8192;
 
 // Waves per workgroup of the per-sequence path for this batch, or 0 for the
-// split path.
-int seq_waves(int32_t B, int32_t Hq, int32_t max_ctx, int bs) {
+// split path (units of `unit` tokens, `sub` units a block).
+int seq_waves(int32_t B, int32_t Hq, int32_t max_ctx, int unit, int sub) {
   const int64_t pairs = static_cast<int64_t>(B) * Hq;
-  const int64_t blocks = ctx_blocks_of(max_ctx, bs);
+  const int64_t units = ctx_units_of(max_ctx, unit);
   for (int w : {4, 8}) {
-    if (pairs * w >= kSeqMinWaves && (blocks + w - 1) / w <= 64 * kSeqTR) return w;
+    if (pairs * w >= kSeqMinWaves && run_blocks((units + w - 1) / w, sub) <= 64 * kSeqTR) return w;
   }
   return 0;
 }
 
-// A (block, head) tile must cover at least one 1 KiB wave load.
+// A streamed unit must cover at least one 1 KiB wave load.
 template <int D, bool FP8, int BS>
-constexpr bool kTileFits = BS * D * (FP8 ? 1 : 2) >= 1024;
+constexpr bool kTileFits = (BS < 16 ? BS : 16) * D * (FP8 ? 1 : 2) >= 1024;
 
 template <int D, bool FP8, int BS>
 hipError_t launch_decode_typed(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
@@ -368,14 +372,15 @@ hipError_t launch_decode_typed(const KvDesc& c, const void* q, int32_t Hq, const
   } else {
     constexpr int kU = FP8 ? kSeqUF8 : kSeqUF16;
     constexpr bool kPipe = FP8 ? kSeqPipeF8 : kSeqPipeF16;
-    const int sw = seq_waves(B, Hq, max_ctx, BS);
+    using G = Geom<D, FP8, BS>;
+    const int sw = seq_waves(B, Hq, max_ctx, G::kUnit, G::kSub);
     if (sw == 4)
       return run_seq<D, FP8, kU, kPipe, 4, kSeqTR, BS>(c, q, Hq, tables, lens, cached, B, max_blocks,
                                                        max_ctx, scale, out, s);
     if (sw == 8)
       return run_seq<D, FP8, kU, kPipe, 8, kSeqTR, BS>(c, q, Hq, tables, lens, cached, B, max_blocks,
                                                        max_ctx, scale, out, s);
-    constexpr int kSplit = kSplitTokens / BS;
+    constexpr int kSplit = kSplitTokens / G::kUnit;  // units per split
     constexpr int kSU = FP8 ? kUF8 : kUF16;
     constexpr bool kSPipe = FP8 ? kPipeF8 : kPipeF16;
     constexpr int kWpg = FP8 ? kWpgF8 : kWpgF16;
@@ -432,6 +437,9 @@ hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32
                                  workspace, s);
     case 32:
       return launch_decode_bs<32>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
+                                  workspace, s);
+    case 64:
+      return launch_decode_bs<64>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
                                   workspace, s);
     default:
       return launch_decode_bs<16>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,

@@ -13,18 +13,29 @@ namespace {
 
 using namespace dev;
 
-// Layout of one (block, head) tile of BS tokens for the wave's loads.
+// Layout of one (block, head) tile of BS tokens for the wave's loads.  The
+// tile is streamed in units of kUnit tokens (the whole tile for BS <= 16,
+// else 16-token slices: rows 16 j .. 16 j + 15 of a tile are contiguous), so
+// the registers a step holds do not grow with the block size.
 template <int D, bool FP8, int BS = 16>
 struct Geom {
   static constexpr int kBytes = FP8 ? 1 : 2;
   static constexpr int kEpl = 16 / kBytes;      // values per lane per 16-byte load
   static constexpr int kLpr = D / kEpl;         // lanes per token row
   static constexpr int kRpi = 64 / kLpr;        // token rows per 1 KiB load
-  static constexpr int kIpb = BS / kRpi;        // loads per block tile
-  static constexpr int kTile = BS * D * kBytes;
+  static constexpr int kUnit = BS < 16 ? BS : 16;  // tokens per streamed unit
+  static constexpr int kSub = BS / kUnit;          // units per block
+  static constexpr int kIpb = kUnit / kRpi;        // loads per unit
+  static constexpr int kTile = BS * D * kBytes;    // one (block, head) tile
+  static constexpr int kUnitBytes = kUnit * D * kBytes;
   static_assert(kLpr >= 4 && kLpr <= 16, "row group must fit a DPP row");
-  static_assert(kIpb >= 1 && BS % kRpi == 0, "tile smaller than one load");
+  static_assert(kIpb >= 1 && kUnit % kRpi == 0, "unit smaller than one load");
+  static_assert((kSub & (kSub - 1)) == 0, "units per block must be a power of two");
 };
+
+// Most blocks a run of u >= 1 consecutive units can touch, sub units a block
+// (a run may start on any unit of its first block).
+__host__ __device__ constexpr int64_t run_blocks(int64_t u, int sub) { return 1 + (u + sub - 2) / sub; }
 
 // q . k for the lane's kEpl values.
 template <bool FP8>
@@ -101,7 +112,7 @@ __device__ __forceinline__ void axpy<true>(float* acc, float p, const u32x4_t& v
   }
 }
 
-// K and V tiles of kU blocks held in registers.
+// K and V of kU units held in registers.
 template <int D, bool FP8, int kU, int BS>
 struct Tiles {
   u32x4_t k[kU][Geom<D, FP8, BS>::kIpb];
@@ -146,30 +157,33 @@ __device__ __forceinline__ u32x4_t load_kv(const uint8_t* p) {
   else return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// One wave's pass over nb >= 1 blocks of one (sequence, head): logical blocks
-// blk0 .. blk0 + nb - 1, physical ids in tb, context length L (tokens at or
-// past L are masked).  kbase / vbase point at the (block 0, kv head) tile plus
-// the lane's 16-byte offset.  Leaves the online-softmax state in sm.  kNT
-// picks the load flavour (load_kv).
+// One wave's pass over nb >= 1 units of one (sequence, head): logical units
+// u0 .. u0 + nb - 1 (unit u is slice u % kSub of logical block u / kSub);
+// lane j of tb holds the physical id of logical block u0 / kSub + j (64 per
+// register); context length L (tokens at or past L are masked).  kbase /
+// vbase point at the (block 0, kv head) tile plus the lane's 16-byte offset.
+// Leaves the online-softmax state in sm.  kNT picks the load flavour
+// (load_kv).
 template <int D, bool FP8, int kU, bool kPipe, int kTR, bool kNT, int BS>
 __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&tb)[kTR], int nb,
-                                              int blk0, int L, const uint8_t* kbase,
+                                              int u0, int L, const uint8_t* kbase,
                                               const uint8_t* vbase, int64_t blk_stride,
                                               float qk_scale, int row, Softmax<D, FP8>& sm) {
   using G = Geom<D, FP8, BS>;
 
-  // Issue the loads of blocks j .. j+kU-1 of the run (past-the-end slots
-  // reload the last block and are masked when consumed).
+  // Issue the loads of units j .. j+kU-1 of the run (past-the-end slots
+  // reload the last unit and are masked when consumed).
   auto issue = [&](Tiles<D, FP8, kU, BS>& t, int j) {
     int64_t off[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int jj = min(j + u, nb - 1);  // wave-uniform
+      const int lu = u0 + min(j + u, nb - 1);              // wave-uniform
+      const int bi = lu / G::kSub - u0 / G::kSub;          // block slot in tb
       int src = tb[0];
 #pragma unroll
-      for (int r = 1; r < kTR; ++r) src = (jj >= r * 64) ? tb[r] : src;
-      const int phys = __builtin_amdgcn_readlane(src, jj & 63);
-      off[u] = static_cast<int64_t>(phys) * blk_stride;
+      for (int r = 1; r < kTR; ++r) src = (bi >= r * 64) ? tb[r] : src;
+      const int phys = __builtin_amdgcn_readlane(src, bi & 63);
+      off[u] = static_cast<int64_t>(phys) * blk_stride + (lu % G::kSub) * G::kUnitBytes;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -191,12 +205,12 @@ __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&t
       for (int i = 0; i < G::kIpb; ++i) s[u][i] = group_sum<G::kLpr>(qr.dot(t.k[u][i])) * qk_scale;
     // Only the step holding the end of the run or of the context has rows to
     // mask (tokens at or past L, past-the-end block slots): a uniform branch.
-    if (j + kU > nb || (blk0 + j + kU) * BS > L) {
+    if (j + kU > nb || (u0 + j + kU) * G::kUnit > L) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
 #pragma unroll
         for (int i = 0; i < G::kIpb; ++i) {
-          const int tok = (blk0 + j + u) * BS + i * G::kRpi + row;
+          const int tok = (u0 + j + u) * G::kUnit + i * G::kRpi + row;
           if (!((j + u < nb) && (tok < L))) {
             s[u][i] = -INFINITY;
             t.v[u][i] = u32x4_t{0u, 0u, 0u, 0u};  // stale rows may hold non-finite bits
@@ -280,8 +294,8 @@ __device__ __forceinline__ int length_rank(int Lb, int lane, int B) {
 // grid (B * Hq), block kW * 64.  Workgroup g serves head h = g % Hq of the
 // sequence of rank g / Hq in the longest-first order (B <= 64; beyond that the
 // sequences keep their index order).  Wave w streams blocks
-// [w nblk / kW, (w + 1) nblk / kW) of the context; at most 64 * kTR blocks per
-// wave (checked by the host).
+// units [w n / kW, (w + 1) n / kW) of the context's n units; at most 64 * kTR
+// blocks per wave (checked by the host).
 template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
 __device__ __forceinline__ void decode_seq_body(
     int g, const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
@@ -309,14 +323,16 @@ __device__ __forceinline__ void decode_seq_body(
   const int kvh = h / (Hq / Hkv);
   const int col = lane % G::kLpr;
   const int row = lane / G::kLpr;
-  const int nblk = (L + BS - 1) / BS;
-  const int blk0 = static_cast<int>(static_cast<int64_t>(w) * nblk / kW);
-  const int nb = static_cast<int>(static_cast<int64_t>(w + 1) * nblk / kW) - blk0;
+  const int nunit = (L + G::kUnit - 1) / G::kUnit;
+  const int u0 = static_cast<int>(static_cast<int64_t>(w) * nunit / kW);
+  const int nb = static_cast<int>(static_cast<int64_t>(w + 1) * nunit / kW) - u0;
 
   Softmax<D, FP8> sm;
   if (nb > 0) {
+    const int b0 = u0 / G::kSub;
     int tb[kTR];
-    load_block_ids<kTR>(tb, tables + static_cast<int64_t>(b) * max_blocks, blk0, nb, lane);
+    load_block_ids<kTR>(tb, tables + static_cast<int64_t>(b) * max_blocks, b0,
+                        (u0 + nb - 1) / G::kSub - b0 + 1, lane);
     QReg<FP8> qr;
     qr.load(q + bh * D + col * G::kEpl);
     clamp_block_ids<kTR>(tb, num_blocks);
@@ -324,10 +340,10 @@ __device__ __forceinline__ void decode_seq_body(
     const uint8_t* vb = vc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
     const int64_t stride = static_cast<int64_t>(Hkv) * G::kTile;
     // a run that starts inside the sequence's shared prefix reads through the caches
-    if (cached != nullptr && blk0 < cached[b])
-      stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+    if (cached != nullptr && b0 < cached[b])
+      stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
     else
-      stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, blk0, L, kb, vb, stride, qk_scale, row, sm);
+      stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
   }
   const float l = sum_rows<D, FP8>(sm);
 

@@ -19,7 +19,7 @@ namespace {
 
 using namespace dev;
 
-// per-sequence decode inside the mixed launch: 2 blocks per step, not
+// per-sequence decode inside the mixed launch: 2 units per step, not
 // pipelined, 4 waves (the standalone fp16 per-sequence configuration)
 constexpr int kMixU = 2;
 constexpr int kMixW = 4;
@@ -68,8 +68,10 @@ template <int BS>
 hipError_t launch_mixed_bs(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
                            const MixedDecode& d, hipStream_t s) {
   // blocks per decode wave decide the block-id registers (64 per register)
+  using G = Geom<128, false, BS>;
   const int64_t ctx = std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * BS, d.max_ctx);
-  const int64_t per_wave = ((ctx + BS - 1) / BS + kMixW - 1) / kMixW;
+  const int64_t units = (ctx + G::kUnit - 1) / G::kUnit;
+  const int64_t per_wave = run_blocks((units + kMixW - 1) / kMixW, G::kSub);
   const int tr = per_wave <= 64 ? 1 : per_wave <= 128 ? 2 : 4;
   if (c.head_dim == 128) {
     if (tr == 1) return run_mixed<128, 1, BS>(c, Hq, scale, p, d, s);
@@ -83,8 +85,14 @@ hipError_t launch_mixed_bs(const KvDesc& c, int32_t Hq, float scale, const Mixed
 
 }  // namespace
 
-// A decode wave holds up to 4 block-id registers of 64 ids each.
-int32_t mixed_max_context(int32_t block_size) { return 64 * 4 * kMixW * block_size; }
+// A decode wave holds up to 4 block-id registers of 64 ids each: the longest
+// context whose per-wave run of units touches at most 256 blocks.
+int32_t mixed_max_context(int32_t block_size) {
+  const int unit = block_size < 16 ? block_size : 16;
+  const int sub = block_size / unit;
+  const int units_per_wave = sub == 1 ? 256 : 255 * sub + 1;
+  return kMixW * units_per_wave * unit;
+}
 
 hipError_t launch_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
                         const MixedDecode& d, hipStream_t s) {
@@ -93,6 +101,8 @@ hipError_t launch_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPre
       return launch_mixed_bs<8>(c, Hq, scale, p, d, s);
     case 32:
       return launch_mixed_bs<32>(c, Hq, scale, p, d, s);
+    case 64:
+      return launch_mixed_bs<64>(c, Hq, scale, p, d, s);
     default:
       return launch_mixed_bs<16>(c, Hq, scale, p, d, s);
   }

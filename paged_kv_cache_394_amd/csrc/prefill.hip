@@ -9,8 +9,8 @@
 // (v_mfma_f32_16x16x32_f16).
 //
 // Tiling.  A workgroup owns 128 query rows of one (sequence, head): 4 wave64s of
-// 32 rows (two 16-row sub-tiles).  Keys are walked in tiles of 64 (8, 4 or 2
-// blocks of 8, 16 or 32 tokens looked up in the block table), staged through LDS: K row-major, V
+// 32 rows (two 16-row sub-tiles).  Keys are walked in tiles of 64 (8, 4, 2 or 1
+// blocks of 8, 16, 32 or 64 tokens looked up in the block table), staged through LDS: K row-major, V
 // transposed, so both MFMA operands are read as 16-byte LDS runs.
 // Each wave computes S^T = K Q^T (so a lane ends up holding the scores of one
 // query row, which makes the row max / sum and the output rescale lane-local up
@@ -84,6 +84,9 @@ hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t to
                                   scale, out, s);
     case 32:
       return launch_prefill_bs<32>(c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, max_chunk,
+                                   scale, out, s);
+    case 64:
+      return launch_prefill_bs<64>(c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, max_chunk,
                                    scale, out, s);
     default:
       return launch_prefill_bs<16>(c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, max_chunk,

@@ -130,7 +130,7 @@ __device__ __forceinline__ TileBlocks tile_blocks(const int32_t* __restrict__ tr
 // q = 2 w + lane / (D/4) (pair p = q / 4, group g = q % 4) for columns
 // 4 dq .. 4 dq + 3, dq = lane % (D/4): keys 32 p + 16 hb + 4 g + i (hb < 2,
 // i < 4), rows of block (32 p + 16 hb + 4 g) / BS -- the same block for the
-// whole wave at each hb, for every block size 8, 16 and 32.
+// whole wave at each hb, for every block size 8, 16, 32 and 64.
 template <int D, int BS>
 struct StageGeom {
   int k_row;    // the chunk's key within the tile, for i = 0 (adds 256 i / CPR)
@@ -151,7 +151,7 @@ struct StageGeom {
     dq = lane % (D / 4);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
-      v_off[hb] = (kvh * BS + (16 * hb + 4 * (vq & 3)) % BS) * D + 4 * dq;
+      v_off[hb] = (kvh * BS + (32 * (vq >> 2) + 16 * hb + 4 * (vq & 3)) % BS) * D + 4 * dq;
   }
 };
 

@@ -68,11 +68,11 @@ def test_device_entry_points_reject_bad_arguments_without_touching_a_gpu():
     d2 = pa.pa_kv_cache(16, 16, 4, 16, 1, 96, 0, 1.0, 1.0)
     st = pa.lib.pa_decode(ctypes.byref(d2), None, 1, None, None, None, 1, 1, 16, 1.0, None, None, 0, None)
     assert st == pa.PA_ERR_UNSUPPORTED
-    for bs in (4, 12, 64):
+    for bs in (4, 12, 128):
         d3 = pa.pa_kv_cache(16, 16, 4, bs, 1, 128, 0, 1.0, 1.0)
         st = pa.lib.pa_write_kv(ctypes.byref(d3), None, None, None, 0, None, 0, None)
         assert st == pa.PA_ERR_UNSUPPORTED and b"block_size" in pa.lib.pa_last_error()
-    for bs in (8, 16, 32):  # zero tokens and no pairs: a valid no-op at every built block size
+    for bs in (8, 16, 32, 64):  # zero tokens and no pairs: a valid no-op at every built block size
         d3 = pa.pa_kv_cache(16, 16, 4, bs, 1, 128, 0, 1.0, 1.0)
         assert pa.lib.pa_write_kv(ctypes.byref(d3), None, None, None, 0, None, 0, None) == pa.PA_OK
     # an e4m3 tile of 8 tokens x 64 dims is 512 bytes: below the 1 KiB the fp8 loads assume

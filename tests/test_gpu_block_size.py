@@ -1,4 +1,4 @@
-"""Block sizes 8, 16 and 32 ([p1] "PagedAttention" and "Block Size": the
+"""Block sizes 8, 16, 32 and 64 ([p1] "PagedAttention" and "Block Size": the
 block size is a tuning knob; smaller blocks waste fewer slots, larger ones
 give the kernel longer contiguous runs).  Decode (split and per-sequence
 paths, fp16 and e4m3), chunked prefill and the mixed step at each block size
@@ -14,7 +14,7 @@ from gpu_harness import ATOL8, DecodeCase, Mixed, PrefillCase, close, oracle_dec
 
 pytestmark = pytest.mark.gpu
 
-SIZES = [8, 16, 32]
+SIZES = [8, 16, 32, 64]
 
 
 def full_ref(case, fp8_ref=None):

@@ -52,7 +52,7 @@ def run_script(w, fp8, script, block_size=16):
     return cache, ocache
 
 
-@pytest.mark.parametrize("block_size", [8, 16, 32])
+@pytest.mark.parametrize("block_size", [8, 16, 32, 64])
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
 def test_scatter_and_cow_bit_exact(fp8, D, block_size):

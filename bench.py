@@ -545,6 +545,75 @@ def _read_counter_csv(path, counter):
     return out
 
 
+def _short_kernel(n):
+    if n.startswith("void at::native::vectorized_elementwise_kernel<8, at::native::neg"):
+        return "torch neg (elementwise copy)"
+    if "FillFunctor" in n:
+        return "torch fill"
+    m = re.match(r"_ZN2pa12_GLOBAL__N_1\d+(\w+?)(I.*)$", n)
+    if m:
+        return f"pa::{m.group(1)} {m.group(2)[:60]}"
+    return n[:70]
+
+
+def summarize_trace(trace_dir, bench_log, out_md):
+    """Write the kernel-time summary from a rocprofv3 --kernel-trace run of this
+    script (its kernel_trace CSV) and the JSON line the same run printed."""
+    trace_csv = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True),
+                       key=os.path.getmtime)[-1]
+    groups = {}   # one row per kernel and grid size: one kernel's workloads stay apart
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    rows = [{"name": n, "wgs": w, "calls": len(d), "avg": sum(d) / len(d), "min": min(d), "max": max(d),
+             "total": sum(d)} for (n, w), d in groups.items()]
+    rows.sort(key=lambda r: -r["total"])
+    everything = sum(r["total"] for r in rows)
+    rows = [r for r in rows if r["total"] > 0.002 * everything]
+    total = sum(r["total"] for r in rows)
+    with open(bench_log) as f:
+        b = json.loads([line for line in f if line.startswith("{")][-1])
+    roof, pc, pf, f8 = b["roofline"], b.get("prefix_cow", {}), b.get("prefill", {}), b.get("fp8_decode", {})
+    body = f"""# Kernel trace: bench.py on llama13b_decode (+ fp8, prefix-sharing, mixed, prefill, block-size legs)
+
+Commands (repository root, GPU box):
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_decode -o run -- python -u bench.py --steps 20 --warmup 3 --no-cpu-baseline > gpurun_out/prof_decode.log
+    python bench.py --summarize-trace gpurun_out/prof_decode gpurun_out/prof_decode.log {out_md}
+
+Template arguments of the decode kernels: <head_dim, e4m3, units per step, pipelined, waves per
+workgroup, block-id registers, block size>.  decode_seq_kernel<128,0,2,0,4,1,16> is the fp16
+13B-shaped decode (the roofline kernel); <128,1,4,0,4,1,16> the e4m3 one; <128,0,2,0,8,1,16> the
+800-token shared-prompt decode (32 x 40 pairs, 8 waves per workgroup; timed without and with the
+shared-prefix hint, so its row averages both); the block-size legs add the same kernels at block
+sizes 8, 32 and 64.  prefill_kernel<head_dim, block size> with 1280 workgroups is the 8 x 512-row
+chunked prefill; mixed_step_kernel runs that prefill and the 13B-shaped decode in one launch.
+
+One row per kernel and grid size (workgroups); rows under 0.2% of GPU time are left out.  Call
+counts include each leg's untimed settle phase.
+
+| kernel | workgroups | calls | average us | min us | max us | share of GPU time |
+|---|---|---|---|---|---|---|
+"""
+    for r in rows:
+        body += (f"| `{_short_kernel(r['name'])}` | {r['wgs']} | {r['calls']} | {r['avg'] / 1e3:.1f} | "
+                 f"{r['min'] / 1e3:.1f} | {r['max'] / 1e3:.1f} | {100 * r['total'] / total:.1f}% |\n")
+    body += f"""
+bench.py's HIP-event figures in the same profiled session:
+- fp16 decode (roofline kernel): mean {roof['ms_mean'] * 1e3:.1f} us, median {roof['ms_median'] * 1e3:.1f} us
+- e4m3 decode: mean {f8.get('pa_decode_ms', 0) * 1e3:.1f} us
+- shared-prompt decode: {pc.get('pa_decode_ms_without_hint', 0) * 1e3:.1f} us streaming every block, {pc.get('pa_decode_ms', 0) * 1e3:.1f} us with the shared-prefix hint
+- chunked prefill: mean {pf.get('ms', 0) * 1e3:.1f} us
+
+The write_kv and copyBuffer rows are dominated by the set-up writes of whole contexts, not by the
+64-token step writes.
+"""
+    with open(out_md, "w") as f:
+        f.write(body)
+    print(body)
+
+
 def summarize_pmc(fetch_dir, write_dir):
     """Write the traffic summary from two rocprofv3 --pmc runs of --pmc-run."""
     def find(d):
@@ -609,9 +678,13 @@ def main():
     ap.add_argument("--pmc-run", action="store_true", help="copy + decode only, for counter runs")
     ap.add_argument("--prefill-only", action="store_true", help="the chunked-prefill leg only (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "BENCH_LOG", "OUT_MD"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library runs on a single MI355X and has no "

@@ -335,6 +335,31 @@ pa_status pa_decode(const pa_kv_cache *cache, const void *q, int32_t num_heads,
                     int32_t max_context_len, float scale, float *out_dev, void *workspace_dev,
                     size_t workspace_bytes, void *hip_stream);
 
+/* One decode step in one launch: append each sequence's new token to the
+ * cache and attend over the context that ends with it ([p1] "PagedAttention
+ * Mechanism" and [p2] "Deep dive": each generated token's K/V goes into the
+ * sequence's last block, then attention reads the blocks through the table).
+ * Same result, bit for bit, as pa_write_kv of the new tokens followed by
+ * pa_decode, with one launch instead of two: the kernel writes the new rows
+ * and takes them from registers for the attention.
+ * The new token of sequence b is its token lens[b] - 1 (lens clamped as in
+ * pa_decode); the caller has already reserved its slot (pa_alloc_append with
+ * n_tokens = 1, then pa_block_tables), so its row goes to physical block
+ * tables[b][(lens[b]-1) / block_size], row (lens[b]-1) % block_size.  A sequence
+ * with lens[b] == 0 appends nothing.  k_new, v_new: device fp16
+ * [B][num_kv_heads][head_dim] (e4m3 caches store them with the cache's scales,
+ * encoded as by pa_write_kv).  cow_pairs_host / n_cow: the copy-on-write pairs
+ * of the reservation, copied on the stream before the launch (the last block
+ * must not be shared when it is written).  Other arguments as for pa_decode.
+ * Errors: as pa_decode, plus BAD_ARG for NULL or unaligned k_new / v_new and
+ * for bad cow pairs. */
+pa_status pa_decode_append(const pa_kv_cache *cache, const void *q, int32_t num_heads,
+                           const void *k_new, const void *v_new, const int32_t *tables_dev,
+                           const int32_t *lens_dev, const int32_t *cached_blocks_dev, int32_t B,
+                           int32_t max_blocks, int32_t max_context_len, float scale,
+                           float *out_dev, void *workspace_dev, size_t workspace_bytes,
+                           const int32_t *cow_pairs_host, int32_t n_cow, void *hip_stream);
+
 /* Chunked-prefill attention over the paged cache ([p1] "Chunked Prefill" and
  * "Mechanics of Chunked Prefill"): the chunk's K/V must already be written (by
  * pa_write_kv).  Sequence b owns query rows cu_q[b] .. cu_q[b+1]-1; row i of it sits

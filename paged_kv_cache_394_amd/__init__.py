@@ -109,6 +109,12 @@ _SIGNATURES = {
                                    ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_decode_append": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          _i32p, ctypes.c_int32, ctypes.c_void_p]),
     "pa_prefill_chunk": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
@@ -360,6 +366,27 @@ def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch
                          _dev(tables, torch.int32), _dev(lens, torch.int32), cb, B, tables.shape[1],
                          max_context_len, scale, _dev(out, torch.float32), ws_ptr, ws_bytes,
                          _stream(stream)))
+
+
+def pa_decode_append(cache: KvCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                     tables: torch.Tensor, lens: torch.Tensor, max_context_len: int, scale: float,
+                     out: torch.Tensor, workspace: Optional[torch.Tensor] = None, cow_pairs=None,
+                     stream=None, cached_blocks: Optional[torch.Tensor] = None) -> None:
+    """One decode step in one launch: sequence b's new token (its token
+    lens[b] - 1, slot already reserved) gets k_new[b] / v_new[b] ([B][Hkv][D]
+    float16, device) written to the cache, and the step attends over the
+    context ending with it.  Other arguments as pa_decode; cow_pairs as
+    pa_write_kv."""
+    B, Hq, D = q.shape
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    cb = None if cached_blocks is None else _dev(cached_blocks, torch.int32)
+    pairs = _i32(cow_pairs if cow_pairs is not None else np.zeros((0, 2))).reshape(-1, 2)
+    _check(lib.pa_decode_append(ctypes.byref(cache.desc), _dev(q, torch.float16), Hq,
+                                _dev(k_new, torch.float16), _dev(v_new, torch.float16),
+                                _dev(tables, torch.int32), _dev(lens, torch.int32), cb, B,
+                                tables.shape[1], max_context_len, scale, _dev(out, torch.float32),
+                                ws_ptr, ws_bytes, _p(pairs) if len(pairs) else None, len(pairs),
+                                _stream(stream)))
 
 
 def pa_prefill_chunk(cache: KvCache, q: torch.Tensor, cu_q: torch.Tensor, prior: torch.Tensor,

@@ -98,6 +98,19 @@ pa_status check_prefill(const pa::KvDesc& d, const std::string& fn, int32_t num_
   return PA_OK;
 }
 
+// Copy-on-write pairs: host int32[n][2], distinct in-pool ids.
+pa_status check_cow(const pa::KvDesc& d, const std::string& fn, const int32_t* pairs, int32_t n) {
+  if (n < 0) return fail(PA_ERR_BAD_ARG, fn + ": negative count");
+  if (n == 0) return PA_OK;
+  if (pairs == nullptr) return fail(PA_ERR_BAD_ARG, fn + ": NULL cow pairs");
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = pairs[2 * i], t = pairs[2 * i + 1];
+    if (s < 0 || s >= d.num_blocks || t < 0 || t >= d.num_blocks || s == t)
+      return fail(PA_ERR_BAD_ARG, fn + ": cow pair out of range");
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,14 +129,7 @@ pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v
     return fail(PA_ERR_BAD_ARG, "pa_write_kv: k_new / v_new must be 16-byte aligned");
   if (static_cast<int64_t>(T) * d.num_kv_heads * (d.head_dim / 8) >= (int64_t(1) << 31) * 256)
     return fail(PA_ERR_BAD_ARG, "pa_write_kv: too many tokens for one launch");
-  if (n_cow > 0) {
-    if (cow_pairs_host == nullptr) return fail(PA_ERR_BAD_ARG, "pa_write_kv: NULL cow pairs");
-    for (int32_t i = 0; i < n_cow; ++i) {
-      const int32_t s = cow_pairs_host[2 * i], t = cow_pairs_host[2 * i + 1];
-      if (s < 0 || s >= d.num_blocks || t < 0 || t >= d.num_blocks || s == t)
-        return fail(PA_ERR_BAD_ARG, "pa_write_kv: cow pair out of range");
-    }
-  }
+  if (pa_status st = check_cow(d, fn, cow_pairs_host, n_cow); st != PA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (n_cow > 0) {
     const hipError_t e = pa::launch_copy_blocks(d, cow_pairs_host, n_cow, s);
@@ -153,6 +159,37 @@ pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
   return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, cached_blocks_dev, B,
                                       max_blocks, max_context_len, scale, out_dev, workspace_dev,
                                       static_cast<hipStream_t>(hip_stream)),
+                    fn);
+}
+
+pa_status pa_decode_append(const pa_kv_cache* cache, const void* q, int32_t num_heads,
+                           const void* k_new, const void* v_new, const int32_t* tables_dev,
+                           const int32_t* lens_dev, const int32_t* cached_blocks_dev, int32_t B,
+                           int32_t max_blocks, int32_t max_context_len, float scale, float* out_dev,
+                           void* workspace_dev, size_t workspace_bytes,
+                           const int32_t* cow_pairs_host, int32_t n_cow, void* hip_stream) {
+  const char* fn = "pa_decode_append";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  if (pa_status st = check_decode(d, fn, num_heads, q, tables_dev, lens_dev, B, max_blocks,
+                                  max_context_len, scale, out_dev, workspace_dev, workspace_bytes);
+      st != PA_OK)
+    return st;
+  if (B > 0 && (k_new == nullptr || v_new == nullptr))
+    return fail(PA_ERR_BAD_ARG, std::string(fn) + ": NULL k_new / v_new");
+  if (B > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(PA_ERR_BAD_ARG, std::string(fn) + ": k_new / v_new must be 16-byte aligned");
+  if (pa_status st = check_cow(d, fn, cow_pairs_host, n_cow); st != PA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (n_cow > 0) {
+    const hipError_t e = pa::launch_copy_blocks(d, cow_pairs_host, n_cow, s);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  if (B == 0) return pa::ok();
+  const pa::DecodeAppend append{k_new, v_new};
+  return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, cached_blocks_dev, B,
+                                      max_blocks, max_context_len, scale, out_dev, workspace_dev, s,
+                                      &append),
                     fn);
 }
 

@@ -120,14 +120,16 @@ __device__ __forceinline__ UnitPos longest_first_unit(int f, const int32_t* __re
 //   qk_scale = softmax scale * log2(e) * k_scale;  v_scale = 1 for fp16.
 //   ctx_cap = min(max_blocks * BS, max_context_len): lengths are clamped to it.
 //   ws_o [B][Hq][nsplit][D], ws_ml [B][Hq][nsplit][2] (max, sum), log2 domain.
-template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst, int BS>
+//   With kAppend, ap carries each sequence's new token (see append_row).
+template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst, int BS,
+          bool kAppend>
 __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
     const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cached, float* __restrict__ out, float* __restrict__ ws_o,
     float* __restrict__ ws_ml, int32_t B, int32_t Hq, int32_t Hkv,
     int32_t max_blocks, int32_t ctx_cap, int32_t nsplit, int32_t num_blocks, float qk_scale,
-    float v_scale) {
+    float v_scale, AppendRows ap) {
   using G = Geom<D, FP8, BS>;
   static_assert(kSplit % kU == 0, "a split is a whole number of steps");
   static_assert(kSplit % G::kSub == 0, "a split is a whole number of blocks");
@@ -175,15 +177,32 @@ __global__ __launch_bounds__(kWPG * 64) void decode_split_kernel(
   }
   const int nb = min(kSplit, nunit - u0);
   const int nsplit_b = (nunit + kSplit - 1) / kSplit;
+  // L >= 1 here; the last split holds token L - 1, reads its new row and
+  // writes it (once per kv head)
+  const bool last_split = kAppend && split == nsplit_b - 1;
+  NewRow nr{};
+  int new_blk = -1;
+  if constexpr (kAppend) {
+    if (last_split) {
+      nr = load_new_row<D, FP8>(ap, b, kvh, Hkv, col);
+      new_blk = block_id_at<kTR>(tb, (L - 1) / BS - b0);
+    }
+  }
   clamp_block_ids<kTR>(tb, num_blocks);
   Softmax<D, FP8> sm;
   const uint8_t* kb = kc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
   const uint8_t* vb = vc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
   const int64_t stride = static_cast<int64_t>(Hkv) * G::kTile;
   if (cached != nullptr && b0 < cached[b])
-    stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
+    stream_blocks<D, FP8, kU, kPipe, kTR, false, BS, kAppend>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale,
+                                                              row, sm, nr);
   else
-    stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
+    stream_blocks<D, FP8, kU, kPipe, kTR, true, BS, kAppend>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale,
+                                                             row, sm, nr);
+  if constexpr (kAppend) {
+    if (last_split && h % (Hq / Hkv) == 0)
+      store_new_row<D, FP8, BS>(ap, nr, new_blk, kvh, Hkv, L, num_blocks, col, row);
+  }
   const float l = sum_rows<D, FP8>(sm);
   if (row != 0) return;
   float* dst;
@@ -285,10 +304,21 @@ int32_t ctx_cap_of(int32_t max_blocks, int32_t max_ctx, int bs) {
 // (one partial per split) does not depend on it.
 constexpr int kSplitTokens = 512;
 
-template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst, int BS>
+// The device-side form of an append request (empty when there is none).
+template <bool FP8>
+AppendRows append_rows(const KvDesc& c, const DecodeAppend* a) {
+  if (a == nullptr) return AppendRows{};
+  return AppendRows{static_cast<const half_t*>(a->k_new), static_cast<const half_t*>(a->v_new),
+                    static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v),
+                    FP8 ? c.k_scale : 1.0f, FP8 ? c.v_scale : 1.0f};
+}
+
+template <int D, bool FP8, int kSplit, int kU, bool kPipe, int kWPG, bool kLongestFirst, int BS,
+          bool kAppend>
 hipError_t run_split(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                      const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
-                     int32_t max_ctx, float scale, float* out, void* workspace, hipStream_t s) {
+                     int32_t max_ctx, float scale, float* out, void* workspace, hipStream_t s,
+                     const DecodeAppend* append) {
   static_assert(kSplit * Geom<D, FP8, BS>::kUnit == kSplitTokens, "a split is kSplitTokens tokens");
   const int64_t nsplit64 = (ctx_units_of(max_ctx, Geom<D, FP8, BS>::kUnit) + kSplit - 1) / kSplit;
   const int32_t nsplit = static_cast<int32_t>(nsplit64);
@@ -299,12 +329,12 @@ hipError_t run_split(const KvDesc& c, const void* q, int32_t Hq, const int32_t* 
   const float qk_scale = scale * kLog2e * (FP8 ? c.k_scale : 1.0f);
   const float v_scale = FP8 ? c.v_scale : 1.0f;
   const uint32_t groups = static_cast<uint32_t>((units + kWPG - 1) / kWPG);
-  decode_split_kernel<D, FP8, kSplit, kU, kPipe, kWPG, kLongestFirst, BS>
+  decode_split_kernel<D, FP8, kSplit, kU, kPipe, kWPG, kLongestFirst, BS, kAppend>
       <<<dim3(groups), dim3(kWPG * 64), 0, s>>>(
           static_cast<const half_t*>(q), static_cast<const uint8_t*>(c.k),
           static_cast<const uint8_t*>(c.v), tables, lens, cached, out, ws_o, ws_ml, B, Hq,
-          c.num_kv_heads,
-          max_blocks, ctx_cap, nsplit, c.num_blocks, qk_scale, v_scale);
+          c.num_kv_heads, max_blocks, ctx_cap, nsplit, c.num_blocks, qk_scale, v_scale,
+          append_rows<FP8>(c, append));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nsplit > 1) {
@@ -316,17 +346,18 @@ hipError_t run_split(const KvDesc& c, const void* q, int32_t Hq, const int32_t* 
   return e;
 }
 
-template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
+template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS, bool kAppend>
 hipError_t run_seq(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                    const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
-                   int32_t max_ctx, float scale, float* out, hipStream_t s) {
+                   int32_t max_ctx, float scale, float* out, hipStream_t s, const DecodeAppend* append) {
   const float qk_scale = scale * kLog2e * (FP8 ? c.k_scale : 1.0f);
   const float v_scale = FP8 ? c.v_scale : 1.0f;
-  decode_seq_kernel<D, FP8, kU, kPipe, kW, kTR, BS>
+  decode_seq_kernel<D, FP8, kU, kPipe, kW, kTR, BS, kAppend>
       <<<dim3(static_cast<uint32_t>(static_cast<int64_t>(B) * Hq)), dim3(kW * 64), 0, s>>>(
           static_cast<const half_t*>(q), static_cast<const uint8_t*>(c.k),
           static_cast<const uint8_t*>(c.v), tables, lens, cached, out, B, Hq, c.num_kv_heads,
-          max_blocks, ctx_cap_of(max_blocks, max_ctx, BS), c.num_blocks, qk_scale, v_scale);
+          max_blocks, ctx_cap_of(max_blocks, max_ctx, BS), c.num_blocks, qk_scale, v_scale,
+          append_rows<FP8>(c, append));
   return hipGetLastError();
 }
 
@@ -362,11 +393,11 @@ int seq_waves(int32_t B, int32_t Hq, int32_t max_ctx, int unit, int sub) {
 template <int D, bool FP8, int BS>
 constexpr bool kTileFits = (BS < 16 ? BS : 16) * D * (FP8 ? 1 : 2) >= 1024;
 
-template <int D, bool FP8, int BS>
+template <int D, bool FP8, int BS, bool kAppend>
 hipError_t launch_decode_typed(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                                const int32_t* lens, const int32_t* cached, int32_t B,
                                int32_t max_blocks, int32_t max_ctx, float scale, float* out,
-                               void* workspace, hipStream_t s) {
+                               void* workspace, hipStream_t s, const DecodeAppend* append) {
   if constexpr (!kTileFits<D, FP8, BS>) {
     return hipErrorInvalidValue;  // rejected by the caller's argument checks
   } else {
@@ -375,35 +406,48 @@ hipError_t launch_decode_typed(const KvDesc& c, const void* q, int32_t Hq, const
     using G = Geom<D, FP8, BS>;
     const int sw = seq_waves(B, Hq, max_ctx, G::kUnit, G::kSub);
     if (sw == 4)
-      return run_seq<D, FP8, kU, kPipe, 4, kSeqTR, BS>(c, q, Hq, tables, lens, cached, B, max_blocks,
-                                                       max_ctx, scale, out, s);
+      return run_seq<D, FP8, kU, kPipe, 4, kSeqTR, BS, kAppend>(c, q, Hq, tables, lens, cached, B,
+                                                                max_blocks, max_ctx, scale, out, s, append);
     if (sw == 8)
-      return run_seq<D, FP8, kU, kPipe, 8, kSeqTR, BS>(c, q, Hq, tables, lens, cached, B, max_blocks,
-                                                       max_ctx, scale, out, s);
+      return run_seq<D, FP8, kU, kPipe, 8, kSeqTR, BS, kAppend>(c, q, Hq, tables, lens, cached, B,
+                                                                max_blocks, max_ctx, scale, out, s, append);
     constexpr int kSplit = kSplitTokens / G::kUnit;  // units per split
     constexpr int kSU = FP8 ? kUF8 : kUF16;
     constexpr bool kSPipe = FP8 ? kPipeF8 : kPipeF16;
     constexpr int kWpg = FP8 ? kWpgF8 : kWpgF16;
     // longest-first unit order needs every length in one wave: B <= 64
     if (B <= 64)
-      return run_split<D, FP8, kSplit, kSU, kSPipe, kWpg, true, BS>(
-          c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s);
-    return run_split<D, FP8, kSplit, kSU, kSPipe, kWpg, false, BS>(
-        c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s);
+      return run_split<D, FP8, kSplit, kSU, kSPipe, kWpg, true, BS, kAppend>(
+          c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s, append);
+    return run_split<D, FP8, kSplit, kSU, kSPipe, kWpg, false, BS, kAppend>(
+        c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s, append);
   }
+}
+
+template <int BS, bool kAppend>
+hipError_t launch_decode_head(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
+                              const int32_t* lens, const int32_t* cached, int32_t B,
+                              int32_t max_blocks, int32_t max_ctx, float scale, float* out,
+                              void* workspace, hipStream_t s, const DecodeAppend* append) {
+#define PA_ARGS c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s, append
+  if (c.head_dim == 128)
+    return c.fp8 ? launch_decode_typed<128, true, BS, kAppend>(PA_ARGS)
+                 : launch_decode_typed<128, false, BS, kAppend>(PA_ARGS);
+  return c.fp8 ? launch_decode_typed<64, true, BS, kAppend>(PA_ARGS)
+               : launch_decode_typed<64, false, BS, kAppend>(PA_ARGS);
+#undef PA_ARGS
 }
 
 template <int BS>
 hipError_t launch_decode_bs(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                             const int32_t* lens, const int32_t* cached, int32_t B,
                             int32_t max_blocks, int32_t max_ctx, float scale, float* out,
-                            void* workspace, hipStream_t s) {
-#define PA_ARGS c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out, workspace, s
-  if (c.head_dim == 128)
-    return c.fp8 ? launch_decode_typed<128, true, BS>(PA_ARGS)
-                 : launch_decode_typed<128, false, BS>(PA_ARGS);
-  return c.fp8 ? launch_decode_typed<64, true, BS>(PA_ARGS) : launch_decode_typed<64, false, BS>(PA_ARGS);
-#undef PA_ARGS
+                            void* workspace, hipStream_t s, const DecodeAppend* append) {
+  if (append != nullptr)
+    return launch_decode_head<BS, true>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale,
+                                        out, workspace, s, append);
+  return launch_decode_head<BS, false>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale,
+                                       out, workspace, s, append);
 }
 
 }  // namespace
@@ -423,7 +467,8 @@ int64_t decode_units(int32_t B, int32_t Hq, int32_t max_context_len) {
 
 hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                          const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
-                         int32_t max_ctx, float scale, float* out, void* workspace, hipStream_t s) {
+                         int32_t max_ctx, float scale, float* out, void* workspace, hipStream_t s,
+                         const DecodeAppend* append) {
   if (B == 0) return hipSuccess;
   if (max_ctx <= 0) {
     // every length is 0: zero output
@@ -434,16 +479,16 @@ hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32
   switch (c.block_size) {
     case 8:
       return launch_decode_bs<8>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
-                                 workspace, s);
+                                 workspace, s, append);
     case 32:
       return launch_decode_bs<32>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
-                                  workspace, s);
+                                  workspace, s, append);
     case 64:
       return launch_decode_bs<64>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
-                                  workspace, s);
+                                  workspace, s, append);
     default:
       return launch_decode_bs<16>(c, q, Hq, tables, lens, cached, B, max_blocks, max_ctx, scale, out,
-                                  workspace, s);
+                                  workspace, s, append);
   }
 }
 

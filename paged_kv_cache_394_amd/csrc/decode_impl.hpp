@@ -112,6 +112,70 @@ __device__ __forceinline__ void axpy<true>(float* acc, float p, const u32x4_t& v
   }
 }
 
+// One lane's 16-byte chunk of a new token's K and V row, in the cache's
+// format.
+struct NewRow {
+  u32x4_t k, v;
+};
+
+// The lane's chunk (kEpl values from src, fp16) of a new token's row in the
+// cache's format: the fp16 bytes, or e4m3 codes with the same encoding as the
+// KV write.
+template <bool FP8>
+__device__ __forceinline__ u32x4_t new_row_chunk(const half_t* src, float scale) {
+  if constexpr (!FP8) {
+    return *reinterpret_cast<const u32x4_t*>(src);
+  } else {
+    const half8_t lo = *reinterpret_cast<const half8_t*>(src);
+    const half8_t hi = *reinterpret_cast<const half8_t*>(src + 8);
+    u32x4_t r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * w + j;  // value e of the chunk is byte e
+        word |= e4m3_quant(static_cast<float>(e < 8 ? lo[e] : hi[e - 8]), scale) << (8 * j);
+      }
+      r[w] = word;
+    }
+    return r;
+  }
+}
+
+// The new tokens of an appending decode: k_new / v_new fp16 [B][Hkv][D]
+// (sequence b's row is its token lens[b] - 1), the cache bases to write them
+// to, and the e4m3 scales used to encode them for an fp8 cache.
+struct AppendRows {
+  const half_t* k_new;
+  const half_t* v_new;
+  uint8_t* k_dst;
+  uint8_t* v_dst;
+  float k_scale, v_scale;
+};
+
+// The lane's chunk of sequence b's new row for kv head kvh.
+template <int D, bool FP8>
+__device__ __forceinline__ NewRow load_new_row(const AppendRows& ap, int b, int kvh, int Hkv, int col) {
+  const int64_t src = (static_cast<int64_t>(b) * Hkv + kvh) * D + col * Geom<D, FP8>::kEpl;
+  return NewRow{new_row_chunk<FP8>(ap.k_new + src, ap.k_scale),
+                new_row_chunk<FP8>(ap.v_new + src, ap.v_scale)};
+}
+
+// The lanes of token row 0 store the new row at token L - 1 (L >= 1) of
+// physical block blk (the table's entry, unclamped: ids outside the pool are
+// skipped, like out-of-range slots in the KV write).
+template <int D, bool FP8, int BS>
+__device__ __forceinline__ void store_new_row(const AppendRows& ap, const NewRow& nr, int blk, int kvh,
+                                              int Hkv, int L, int num_blocks, int col, int row) {
+  using G = Geom<D, FP8, BS>;
+  if (row != 0 || static_cast<uint32_t>(blk) >= static_cast<uint32_t>(num_blocks)) return;
+  const int64_t dst = (static_cast<int64_t>(blk) * Hkv + kvh) * G::kTile +
+                      static_cast<int64_t>((L - 1) % BS) * D * G::kBytes + col * 16;
+  *reinterpret_cast<u32x4_t*>(ap.k_dst + dst) = nr.k;
+  *reinterpret_cast<u32x4_t*>(ap.v_dst + dst) = nr.v;
+}
+
 // K and V of kU units held in registers.
 template <int D, bool FP8, int kU, int BS>
 struct Tiles {
@@ -139,6 +203,15 @@ __device__ __forceinline__ void load_block_ids(int (&tb)[kTR], const int32_t* __
   }
 }
 
+// Entry bi of the block ids a wave loaded (load_block_ids), wave-uniform.
+template <int kTR>
+__device__ __forceinline__ int block_id_at(const int (&tb)[kTR], int bi) {
+  int src = tb[0];
+#pragma unroll
+  for (int r = 1; r < kTR; ++r) src = (bi >= r * 64) ? tb[r] : src;
+  return __builtin_amdgcn_readlane(src, bi & 63);
+}
+
 // Ids outside the pool read as block 0.
 template <int kTR>
 __device__ __forceinline__ void clamp_block_ids(int (&tb)[kTR], int num_blocks) {
@@ -163,12 +236,15 @@ __device__ __forceinline__ u32x4_t load_kv(const uint8_t* p) {
 // register); context length L (tokens at or past L are masked).  kbase /
 // vbase point at the (block 0, kv head) tile plus the lane's 16-byte offset.
 // Leaves the online-softmax state in sm.  kNT picks the load flavour
-// (load_kv).
-template <int D, bool FP8, int kU, bool kPipe, int kTR, bool kNT, int BS>
+// (load_kv).  With kAppend, token L - 1 is a new token whose row is taken
+// from nr instead of the cache (its cache row is being written by the same
+// launch).
+template <int D, bool FP8, int kU, bool kPipe, int kTR, bool kNT, int BS, bool kAppend = false>
 __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&tb)[kTR], int nb,
                                               int u0, int L, const uint8_t* kbase,
                                               const uint8_t* vbase, int64_t blk_stride,
-                                              float qk_scale, int row, Softmax<D, FP8>& sm) {
+                                              float qk_scale, int row, Softmax<D, FP8>& sm,
+                                              const NewRow& nr = NewRow{}) {
   using G = Geom<D, FP8, BS>;
 
   // Issue the loads of units j .. j+kU-1 of the run (past-the-end slots
@@ -198,6 +274,21 @@ __device__ __forceinline__ void stream_blocks(const QReg<FP8>& qr, const int (&t
   };
 
   auto consume = [&](Tiles<D, FP8, kU, BS>& t, int j) {
+    if constexpr (kAppend) {
+      // the step holding token L - 1 (a uniform branch)
+      if ((u0 + j) * G::kUnit < L && L <= (u0 + j + kU) * G::kUnit) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+#pragma unroll
+          for (int i = 0; i < G::kIpb; ++i) {
+            if ((u0 + j + u) * G::kUnit + i * G::kRpi + row == L - 1) {
+              t.k[u][i] = nr.k;
+              t.v[u][i] = nr.v;
+            }
+          }
+        }
+      }
+    }
     float s[kU][G::kIpb];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -296,12 +387,13 @@ __device__ __forceinline__ int length_rank(int Lb, int lane, int B) {
 // sequences keep their index order).  Wave w streams blocks
 // units [w n / kW, (w + 1) n / kW) of the context's n units; at most 64 * kTR
 // blocks per wave (checked by the host).
-template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
+template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS, bool kAppend = false>
 __device__ __forceinline__ void decode_seq_body(
     int g, const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cached, float* __restrict__ out, int32_t B, int32_t Hq, int32_t Hkv,
-    int32_t max_blocks, int32_t ctx_cap, int32_t num_blocks, float qk_scale, float v_scale) {
+    int32_t max_blocks, int32_t ctx_cap, int32_t num_blocks, float qk_scale, float v_scale,
+    const AppendRows& ap = AppendRows{}) {
   using G = Geom<D, FP8, BS>;
   static_assert(kW >= 2 && kW <= 8, "2 to 8 waves per workgroup");
   const int lane = threadIdx.x & 63;
@@ -328,6 +420,13 @@ __device__ __forceinline__ void decode_seq_body(
   const int nb = static_cast<int>(static_cast<int64_t>(w + 1) * nunit / kW) - u0;
 
   Softmax<D, FP8> sm;
+  // only the wave whose run ends with the context's last unit (it holds
+  // token L - 1) reads the new row; it also writes it, once per kv head
+  const bool last_wave = kAppend && nb > 0 && u0 + nb == nunit;
+  NewRow nr{};
+  if constexpr (kAppend) {
+    if (last_wave) nr = load_new_row<D, FP8>(ap, b, kvh, Hkv, col);
+  }
   if (nb > 0) {
     const int b0 = u0 / G::kSub;
     int tb[kTR];
@@ -335,15 +434,25 @@ __device__ __forceinline__ void decode_seq_body(
                         (u0 + nb - 1) / G::kSub - b0 + 1, lane);
     QReg<FP8> qr;
     qr.load(q + bh * D + col * G::kEpl);
+    int new_blk = -1;  // the new token's block, before ids are clamped
+    if constexpr (kAppend) {
+      if (last_wave) new_blk = block_id_at<kTR>(tb, (L - 1) / BS - b0);
+    }
     clamp_block_ids<kTR>(tb, num_blocks);
     const uint8_t* kb = kc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
     const uint8_t* vb = vc + static_cast<int64_t>(kvh) * G::kTile + lane * 16;
     const int64_t stride = static_cast<int64_t>(Hkv) * G::kTile;
     // a run that starts inside the sequence's shared prefix reads through the caches
     if (cached != nullptr && b0 < cached[b])
-      stream_blocks<D, FP8, kU, kPipe, kTR, false, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
+      stream_blocks<D, FP8, kU, kPipe, kTR, false, BS, kAppend>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale,
+                                                                row, sm, nr);
     else
-      stream_blocks<D, FP8, kU, kPipe, kTR, true, BS>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale, row, sm);
+      stream_blocks<D, FP8, kU, kPipe, kTR, true, BS, kAppend>(qr, tb, nb, u0, L, kb, vb, stride, qk_scale,
+                                                               row, sm, nr);
+    if constexpr (kAppend) {
+      if (last_wave && h % (Hq / Hkv) == 0)
+        store_new_row<D, FP8, BS>(ap, nr, new_blk, kvh, Hkv, L, num_blocks, col, row);
+    }
   }
   const float l = sum_rows<D, FP8>(sm);
 
@@ -375,14 +484,16 @@ __device__ __forceinline__ void decode_seq_body(
 }
 
 // One workgroup per (sequence, head); see decode_seq_body.
-template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS>
+template <int D, bool FP8, int kU, bool kPipe, int kW, int kTR, int BS, bool kAppend>
 __global__ __launch_bounds__(kW * 64) void decode_seq_kernel(
     const half_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cached, float* __restrict__ out, int32_t B, int32_t Hq, int32_t Hkv,
-    int32_t max_blocks, int32_t ctx_cap, int32_t num_blocks, float qk_scale, float v_scale) {
-  decode_seq_body<D, FP8, kU, kPipe, kW, kTR, BS>(blockIdx.x, q, kc, vc, tables, lens, cached, out, B, Hq,
-                                              Hkv, max_blocks, ctx_cap, num_blocks, qk_scale, v_scale);
+    int32_t max_blocks, int32_t ctx_cap, int32_t num_blocks, float qk_scale, float v_scale,
+    AppendRows ap) {
+  decode_seq_body<D, FP8, kU, kPipe, kW, kTR, BS, kAppend>(blockIdx.x, q, kc, vc, tables, lens, cached, out,
+                                                         B, Hq, Hkv, max_blocks, ctx_cap, num_blocks,
+                                                         qk_scale, v_scale, ap);
 }
 
 }  // namespace

@@ -29,11 +29,18 @@ int32_t decode_partition_tokens();
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len);
 // Work units (one wave each) of one decode launch; must stay below 2^31.
 int64_t decode_units(int32_t B, int32_t Hq, int32_t max_context_len);
+// The new token of every sequence for an appending decode: k_new / v_new are
+// fp16 [B][Hkv][D]; sequence b's row goes to its token lens[b] - 1.
+struct DecodeAppend {
+  const void* k_new;
+  const void* v_new;
+};
 // cached: NULL or int32[B], leading blocks per sequence read through the caches.
+// append: NULL, or the new tokens written into the cache by the same launch.
 hipError_t launch_decode(const KvDesc& c, const void* q, int32_t Hq, const int32_t* tables,
                          const int32_t* lens, const int32_t* cached, int32_t B, int32_t max_blocks,
                          int32_t max_context_len, float scale, float* out, void* workspace,
-                         hipStream_t s);
+                         hipStream_t s, const DecodeAppend* append = nullptr);
 
 // Chunked prefill (MFMA).
 hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,

@@ -1,0 +1,193 @@
+"""pa_decode_append: the decode step in one launch (append each sequence's new
+token to its last block, then attend).  It must leave the same cache bytes and
+give the same output bits as pa_write_kv followed by pa_decode, on every
+decode path (split, per-sequence with 4 and 8 waves), for fp16 and e4m3
+caches, every block size, grouped heads, empty contexts and a copy-on-write
+reservation; and match the float64 oracle over the whole context."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_394_amd as pa
+import workloads
+from gpu_harness import ATOL8, close, fp8_scales, oracle_decode, pool_geometry
+
+pytestmark = pytest.mark.gpu
+
+
+class Twin:
+    """Two identical (pool, cache) pairs holding every context but its last
+    token, with the last token's slot reserved; the new rows on the device."""
+
+    def __init__(self, w, fp8=False, block_size=16):
+        self.w = w
+        self.fp8 = fp8
+        self.bs = block_size
+        ks, vs = fp8_scales(w, range(w.batch)) if fp8 else (1.0, 1.0)
+        self.scales = (ks, vs)
+        nb, order = pool_geometry(w, block_size)
+        self.sides = []
+        for _ in range(2):
+            pool = pa.pa_pool_create(nb, block_size, order)
+            cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size, fp8=fp8,
+                               k_scale=ks, v_scale=vs, fill=(255 if fp8 else float("nan")))
+            ids, slots = [], []
+            for b in range(w.batch):
+                s = pa.pa_seq_create(pool)
+                ids.append(s)
+                L = int(w.lens[b])
+                if L == 0:
+                    slots.append(-1)
+                    continue
+                k, v = w.kv(b)
+                sl, _ = pa.pa_alloc_append(pool, s, L - 1)
+                if L > 1:
+                    pa.pa_write_kv(cache, torch.from_numpy(k[:L - 1]).cuda(),
+                                   torch.from_numpy(v[:L - 1]).cuda(), torch.from_numpy(sl).cuda())
+                sl, cow = pa.pa_alloc_append(pool, s, 1)
+                assert cow is None
+                slots.append(int(sl[0]))
+            self.sides.append((pool, cache, ids, slots))
+        pool, cache, ids, slots = self.sides[0]
+        self.max_ctx = max(1, int(w.lens.max()))
+        tables, lens = pa.pa_block_tables(pool, ids, -(-self.max_ctx // block_size))
+        assert np.array_equal(lens, w.lens.astype(np.int32))
+        self.tables = torch.from_numpy(tables).cuda()
+        self.lens = torch.from_numpy(lens).cuda()
+        self.slots = torch.tensor(slots, dtype=torch.int32, device="cuda")
+        kn = np.zeros((w.batch, w.num_kv_heads, w.head_dim), np.float16)
+        vn = np.full((w.batch, w.num_kv_heads, w.head_dim), 7.0, np.float16)  # empty contexts: never used
+        for b in range(w.batch):
+            L = int(w.lens[b])
+            if L:
+                k, v = w.kv(b)
+                kn[b], vn[b] = k[L - 1], v[L - 1]
+        self.k_new = torch.from_numpy(kn).cuda()
+        self.v_new = torch.from_numpy(vn).cuda()
+        self.q = torch.from_numpy(np.ascontiguousarray(w.q)).cuda()
+        nbytes = pa.pa_decode_workspace_bytes(w.batch, w.num_heads, w.head_dim, self.max_ctx)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+    def two_calls(self):
+        cache = self.sides[0][1]
+        out = torch.empty((self.w.batch, self.w.num_heads, self.w.head_dim), device="cuda")
+        pa.pa_write_kv(cache, self.k_new, self.v_new, self.slots)
+        pa.pa_decode(cache, self.q, self.tables, self.lens, self.max_ctx, self.w.scale, out, self.ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), cache
+
+    def one_call(self):
+        cache = self.sides[1][1]
+        out = torch.empty((self.w.batch, self.w.num_heads, self.w.head_dim), device="cuda")
+        pa.pa_decode_append(cache, self.q, self.k_new, self.v_new, self.tables, self.lens, self.max_ctx,
+                            self.w.scale, out, self.ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), cache
+
+
+def same_bytes(a: pa.KvCache, b: pa.KvCache):
+    for x, y in ((a.k, b.k), (a.v, b.v)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def check(t: Twin, fp8_source_tol=True):
+    ref_out, ref_cache = t.two_calls()
+    got, cache = t.one_call()
+    assert np.array_equal(got.view(np.uint32), ref_out.view(np.uint32))
+    same_bytes(cache, ref_cache)
+    w = t.w
+    pairs = [(i, h) for i in range(w.batch) for h in range(w.num_heads)]
+    ref = oracle_decode(w, pairs, None, t.scales if t.fp8 else None)
+    R = np.stack([np.stack([ref[(i, h)] for h in range(w.num_heads)]) for i in range(w.batch)])
+    close(got, R)
+    return got
+
+
+@pytest.mark.parametrize("block_size", [8, 16, 32, 64])
+@pytest.mark.parametrize("D,heads", [(128, (8, 2)), (64, (4, 4))])
+def test_split_path(block_size, D, heads):
+    lens = [1, 2, 15, 16, 17, 33, 511, 512, 513, 1100, 0, 2049]
+    w = workloads.custom_decode(301 + D + block_size, lens, heads[0], heads[1], D)
+    got = check(Twin(w, block_size=block_size))
+    assert np.all(got[10] == 0)
+
+
+@pytest.mark.parametrize("block_size", [8, 16, 64])
+@pytest.mark.parametrize("B,H,KVH,D,top", [(64, 32, 8, 128, 1500), (30, 40, 40, 64, 700)])
+def test_per_sequence_paths(block_size, B, H, KVH, D, top):
+    rng = np.random.default_rng(311 + B)
+    lens = rng.integers(1, top, size=B)
+    lens[2] = 0
+    lens[4] = 1
+    w = workloads.custom_decode(311 + B, lens, H, KVH, D)
+    check(Twin(w, block_size=block_size))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_cache(D):
+    lens = [1, 9, 64, 300, 1100, 2000]
+    w = workloads.custom_decode(321 + D, lens, 4, 2, D)
+    check(Twin(w, fp8=True))
+    rng = np.random.default_rng(322)
+    lens = rng.integers(1, 1200, size=64)
+    w = workloads.custom_decode(323 + D, lens, 32, 32, D)   # per-sequence path, e4m3
+    got = check(Twin(w, fp8=True))
+    ref = oracle_decode(w, [(i, 0) for i in range(0, 64, 7)])
+    long_ = [i for i in range(0, 64, 7) if lens[i] >= 200]
+    for i in long_:
+        close(got[i, 0], ref[(i, 0)], ATOL8, ATOL8)
+
+
+def test_copy_on_write_reservation():
+    """A forked sequence whose shared last block is partly filled: the
+    reservation copies the block, and the append writes into the copy."""
+    w = workloads.custom_decode(331, [45, 45], 4, 4, 128)
+    k, v = w.kv(0)
+    outs, caches = [], []
+    for fused in (False, True):
+        pool = pa.pa_pool_create(16, 16)
+        cache = pa.KvCache(16, 4, 128, fill=float("nan"))
+        s0 = pa.pa_seq_create(pool)
+        sl, _ = pa.pa_alloc_append(pool, s0, 44)
+        pa.pa_write_kv(cache, torch.from_numpy(k[:44]).cuda(), torch.from_numpy(v[:44]).cuda(),
+                       torch.from_numpy(sl).cuda())
+        s1 = pa.pa_fork_cow(pool, s0)
+        sl1, cow = pa.pa_alloc_append(pool, s1, 1)
+        assert cow is not None
+        tables, lens = pa.pa_block_tables(pool, [s1], 3)
+        q = torch.from_numpy(np.ascontiguousarray(w.q[:1])).cuda()
+        kn = torch.from_numpy(np.ascontiguousarray(k[44:45])).cuda()
+        vn = torch.from_numpy(np.ascontiguousarray(v[44:45])).cuda()
+        out = torch.empty((1, 4, 128), device="cuda")
+        ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(1, 4, 128, 45)), dtype=torch.uint8,
+                         device="cuda")
+        tt, ll = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+        if fused:
+            pa.pa_decode_append(cache, q, kn, vn, tt, ll, 45, w.scale, out, ws, cow_pairs=[cow])
+        else:
+            pa.pa_write_kv(cache, kn, vn, torch.from_numpy(sl1).cuda(), [cow])
+            pa.pa_decode(cache, q, tt, ll, 45, w.scale, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        caches.append(cache)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    same_bytes(caches[0], caches[1])
+    ref = oracle_decode(w, [(0, h) for h in range(4)])
+    for h in range(4):
+        close(outs[1][0, h], ref[(0, h)])
+
+
+def test_llama13b_batch_sampled():
+    """The full 64-sequence, 40-head batch (the benchmark's step) on the fused
+    path: bitwise equal to the two calls, sampled against the oracle."""
+    w = workloads.llama13b_decode()
+    t = Twin(w)
+    ref_out, ref_cache = t.two_calls()
+    got, cache = t.one_call()
+    assert np.array_equal(got.view(np.uint32), ref_out.view(np.uint32))
+    same_bytes(cache, ref_cache)
+    order = np.argsort(w.lens)
+    pairs = [(int(order[0]), 0), (int(order[-1]), 39), (int(order[-1]), 3), (5, 17), (40, 22)]
+    for (i, h), r in oracle_decode(w, pairs).items():
+        close(got[i, h], r)

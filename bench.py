@@ -440,11 +440,13 @@ def bench_mixed(pa, torch, np, workloads, reps):
             "speedup": round(sep_ms / mixed_ms, 3)}
 
 
-def bench_prefill(pa, torch, np, workloads, reps, block_size=16):
+def bench_prefill(pa, torch, np, workloads, reps, block_size=16, fp8=False):
     w = workloads.chunked_prefill()
     nb, order = pool_geometry(w, block_size, np)
     pool = pa.pa_pool_create(nb, block_size, order)
-    cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size)
+    ks, vs = fp8_scales(w, np) if fp8 else (1.0, 1.0)
+    cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size, fp8=fp8, k_scale=ks,
+                       v_scale=vs)
     ids = []
     for b in range(w.batch):
         s = pa.pa_seq_create(pool)
@@ -470,7 +472,8 @@ def bench_prefill(pa, torch, np, workloads, reps, block_size=16):
     P = w.prior.astype(np.float64)
     flops = 4.0 * w.head_dim * w.num_heads * float(np.sum(C * P + C * (C + 1) / 2))
     tflops = flops / (mean * 1e-3) / 1e12
-    return {"workload": "chunked_prefill: 8 seqs, prior U[0,4096], chunk 512, 40 heads x 128, fp16",
+    return {"workload": "chunked_prefill: 8 seqs, prior U[0,4096], chunk 512, 40 heads x 128, "
+                        + ("e4m3 cache" if fp8 else "fp16"),
             "ms": round(mean, 4),
             "causal_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
             "mfma_util": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
@@ -802,6 +805,9 @@ def main():
         torch.cuda.empty_cache()
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
+        torch.cuda.empty_cache()
+        log("chunked prefill, e4m3 cache")
+        res["prefill_fp8"] = bench_prefill(pa, torch, np, workloads, 20, fp8=True)
         torch.cuda.empty_cache()
         log("block sizes 8 / 32 / 64")
         res["block_sizes"] = bench_block_sizes(pa, torch, np, workloads, w, args.steps, args.warmup,

@@ -267,8 +267,10 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t head_dim,
  * grid holds the prefill workgroups first and the decode workgroups after
  * them, so decode work fills the CUs the prefill's tail leaves idle.
  * prefill / decode: either may be NULL or empty (batch 0); fields as the
- * arguments of the two calls.  fp16 caches (an e4m3 cache allows decode only).
- * The one-launch form covers decode contexts up to 16384 tokens; beyond that,
+ * arguments of the two calls.  fp16 or e4m3 caches.
+ * The one-launch form covers decode contexts up to 4 waves x 256 blocks of
+ * units (8192 / 16384 / 32704 / 65344 tokens at block_size 8 / 16 / 32 / 64);
+ * beyond that,
  * or with one part empty, the parts are launched one after the other on the
  * same stream (same results), which is when decode->workspace may be needed
  * (size as pa_decode_workspace_bytes).  Errors: as the two calls. */
@@ -369,9 +371,11 @@ pa_status pa_decode_append(const pa_kv_cache *cache, const void *q, int32_t num_
  * or beyond it are never read or written).  cu_q_dev: device int32[B+1],
  * non-decreasing, cu_q[0] = 0.  prior_dev: device int32[B].  tables_dev: device
  * int32[B][max_blocks].  max_chunk: upper bound on cu_q[b+1] - cu_q[b].  out_dev:
- * device fp32 [total_q_rows][num_heads][head_dim].
- * Errors: BAD_ARG, UNSUPPORTED (block_size not 8/16/32/64, head_dim not 64/128, e4m3
- * cache), HIP. */
+ * device fp32 [total_q_rows][num_heads][head_dim].  An e4m3 cache is widened to
+ * fp16 on the way to the matrix cores (exact) and its scales are applied to the
+ * scores (k_scale) and the output (v_scale).
+ * Errors: BAD_ARG, UNSUPPORTED (block_size not 8/16/32/64, head_dim not 64/128, an
+ * e4m3 tile under 1 KiB), HIP. */
 pa_status pa_prefill_chunk(const pa_kv_cache *cache, const void *q, int32_t num_heads,
                            int32_t total_q_rows, const int32_t *cu_q_dev, const int32_t *prior_dev,
                            const int32_t *tables_dev, int32_t B, int32_t max_blocks,

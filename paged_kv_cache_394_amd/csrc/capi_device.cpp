@@ -81,7 +81,6 @@ pa_status check_prefill(const pa::KvDesc& d, const std::string& fn, int32_t num_
                         int32_t total_q_rows, const int32_t* cu_q_dev, const int32_t* prior_dev,
                         const int32_t* tables_dev, int32_t B, int32_t max_blocks, int32_t max_chunk,
                         float scale, const float* out_dev) {
-  if (d.fp8) return fail(PA_ERR_UNSUPPORTED, fn + ": e4m3 caches are decode-only");
   if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
     return fail(PA_ERR_BAD_ARG, fn + ": num_heads must be a positive multiple of num_kv_heads");
   if (B < 0 || max_blocks < 1 || max_chunk < 0 || total_q_rows < 0)

@@ -49,7 +49,7 @@ hipError_t launch_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t to
                           hipStream_t s);
 
 // Mixed step: chunked prefill of some sequences and decode of others in one
-// launch (fp16 caches).  The decode half supports contexts up to
+// launch (fp16 or e4m3 caches).  The decode half supports contexts up to
 // mixed_max_context(block_size) tokens; the caller falls back to two launches
 // beyond.
 struct MixedPrefill {

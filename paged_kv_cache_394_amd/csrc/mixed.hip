@@ -19,35 +19,37 @@ namespace {
 
 using namespace dev;
 
-// per-sequence decode inside the mixed launch: 2 units per step, not
-// pipelined, 4 waves (the standalone fp16 per-sequence configuration)
-constexpr int kMixU = 2;
+// per-sequence decode inside the mixed launch: 2 units per step (4 for e4m3),
+// not pipelined, 4 waves (the standalone per-sequence configurations)
+template <bool FP8>
+constexpr int kMixU = FP8 ? 4 : 2;
 constexpr int kMixW = 4;
 static_assert(kMixW * 64 == kThreads, "decode and prefill workgroups have one shape");
 
-template <int D, int kTR, int BS>
+// qk_scale = softmax scale * log2 e (* k_scale for e4m3); v_scale = 1 for fp16.
+template <int D, int kTR, int BS, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void mixed_step_kernel(
-    const half_t* __restrict__ pq, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
-    const int32_t* __restrict__ ptables, float* __restrict__ pout, int32_t Bp, int32_t Hq,
-    int32_t Hkv, int32_t total_q, int32_t pmax_blocks, int32_t num_blocks, int32_t nqt,
-    float qk_scale, int32_t n_prefill_wgs, const half_t* __restrict__ dq,
+    const half_t* __restrict__ pq, const elem_t<FP8>* __restrict__ kc,
+    const elem_t<FP8>* __restrict__ vc, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ prior, const int32_t* __restrict__ ptables, float* __restrict__ pout,
+    int32_t Bp, int32_t Hq, int32_t Hkv, int32_t total_q, int32_t pmax_blocks, int32_t num_blocks,
+    int32_t nqt, float qk_scale, float v_scale, int32_t n_prefill_wgs, const half_t* __restrict__ dq,
     const int32_t* __restrict__ dtables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cached, float* __restrict__ dout, int32_t Bd, int32_t dmax_blocks,
     int32_t ctx_cap) {
   const int wg = blockIdx.x;
   if (wg < n_prefill_wgs) {
-    prefill_body<D, BS>(wg, pq, kc, vc, cu_q, prior, ptables, pout, Bp, Hq, Hkv, total_q, pmax_blocks,
-                    num_blocks, nqt, qk_scale);
+    prefill_body<D, BS, FP8>(wg, pq, kc, vc, cu_q, prior, ptables, pout, Bp, Hq, Hkv, total_q,
+                             pmax_blocks, num_blocks, nqt, qk_scale, v_scale);
   } else {
-    decode_seq_body<D, false, kMixU, false, kMixW, kTR, BS>(
+    decode_seq_body<D, FP8, kMixU<FP8>, false, kMixW, kTR, BS>(
         wg - n_prefill_wgs, dq, reinterpret_cast<const uint8_t*>(kc),
         reinterpret_cast<const uint8_t*>(vc), dtables, lens, cached, dout, Bd, Hq, Hkv, dmax_blocks,
-        ctx_cap, num_blocks, qk_scale, 1.0f);
+        ctx_cap, num_blocks, qk_scale, v_scale);
   }
 }
 
-template <int D, int kTR, int BS>
+template <int D, int kTR, int BS, bool FP8>
 hipError_t run_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
                      const MixedDecode& d, hipStream_t s) {
   const int32_t nqt = (p.max_chunk + kBq - 1) / kBq;
@@ -56,12 +58,25 @@ hipError_t run_mixed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefil
   const int64_t n_decode = static_cast<int64_t>(d.B) * Hq;
   const int32_t ctx_cap =
       static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(d.max_blocks) * BS, d.max_ctx));
-  mixed_step_kernel<D, kTR, BS><<<dim3(static_cast<uint32_t>(n_prefill + n_decode)), dim3(kThreads), 0, s>>>(
-      static_cast<const half_t*>(p.q), static_cast<const half_t*>(c.k),
-      static_cast<const half_t*>(c.v), p.cu_q, p.prior, p.tables, p.out, p.B, Hq, c.num_kv_heads,
-      p.total_q, p.max_blocks, c.num_blocks, nqt, scale * kLog2e, static_cast<int32_t>(n_prefill),
+  mixed_step_kernel<D, kTR, BS, FP8><<<dim3(static_cast<uint32_t>(n_prefill + n_decode)), dim3(kThreads), 0, s>>>(
+      static_cast<const half_t*>(p.q), static_cast<const elem_t<FP8>*>(c.k),
+      static_cast<const elem_t<FP8>*>(c.v), p.cu_q, p.prior, p.tables, p.out, p.B, Hq, c.num_kv_heads,
+      p.total_q, p.max_blocks, c.num_blocks, nqt, scale * kLog2e * (FP8 ? c.k_scale : 1.0f),
+      FP8 ? c.v_scale : 1.0f, static_cast<int32_t>(n_prefill),
       static_cast<const half_t*>(d.q), d.tables, d.lens, d.cached, d.out, d.B, d.max_blocks, ctx_cap);
   return hipGetLastError();
+}
+
+template <int D, int BS, bool FP8>
+hipError_t launch_mixed_typed(const KvDesc& c, int32_t Hq, float scale, const MixedPrefill& p,
+                              const MixedDecode& d, hipStream_t s, int tr) {
+  if constexpr (FP8 && (BS < 16 ? BS : 16) * D < 1024) {
+    return hipErrorInvalidValue;  // an e4m3 unit below 1 KiB is refused by the argument checks
+  } else {
+    if (tr == 1) return run_mixed<D, 1, BS, FP8>(c, Hq, scale, p, d, s);
+    if (tr == 2) return run_mixed<D, 2, BS, FP8>(c, Hq, scale, p, d, s);
+    return run_mixed<D, 4, BS, FP8>(c, Hq, scale, p, d, s);
+  }
 }
 
 template <int BS>
@@ -73,14 +88,10 @@ hipError_t launch_mixed_bs(const KvDesc& c, int32_t Hq, float scale, const Mixed
   const int64_t units = (ctx + G::kUnit - 1) / G::kUnit;
   const int64_t per_wave = run_blocks((units + kMixW - 1) / kMixW, G::kSub);
   const int tr = per_wave <= 64 ? 1 : per_wave <= 128 ? 2 : 4;
-  if (c.head_dim == 128) {
-    if (tr == 1) return run_mixed<128, 1, BS>(c, Hq, scale, p, d, s);
-    if (tr == 2) return run_mixed<128, 2, BS>(c, Hq, scale, p, d, s);
-    return run_mixed<128, 4, BS>(c, Hq, scale, p, d, s);
-  }
-  if (tr == 1) return run_mixed<64, 1, BS>(c, Hq, scale, p, d, s);
-  if (tr == 2) return run_mixed<64, 2, BS>(c, Hq, scale, p, d, s);
-  return run_mixed<64, 4, BS>(c, Hq, scale, p, d, s);
+  if (c.head_dim == 128) return c.fp8 ? launch_mixed_typed<128, BS, true>(c, Hq, scale, p, d, s, tr)
+                                      : launch_mixed_typed<128, BS, false>(c, Hq, scale, p, d, s, tr);
+  return c.fp8 ? launch_mixed_typed<64, BS, true>(c, Hq, scale, p, d, s, tr)
+               : launch_mixed_typed<64, BS, false>(c, Hq, scale, p, d, s, tr);
 }
 
 }  // namespace

@@ -50,26 +50,33 @@ namespace {
 using namespace dev;
 }  // namespace
 
+template <int D, int BS, bool FP8>
+void run_prefill(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q, const int32_t* cu_q,
+                 const int32_t* prior, const int32_t* tables, int32_t B, int32_t max_blocks,
+                 int32_t nqt, float scale, float* out, hipStream_t s) {
+  const int64_t pairs = static_cast<int64_t>(B) * Hq;
+  const dim3 grid(static_cast<uint32_t>((pairs + kXcds - 1) / kXcds * kXcds * nqt));
+  prefill_kernel<D, BS, FP8><<<grid, dim3(kThreads), 0, s>>>(
+      static_cast<const half_t*>(q), static_cast<const elem_t<FP8>*>(c.k),
+      static_cast<const elem_t<FP8>*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
+      max_blocks, c.num_blocks, nqt, scale * kLog2e * (FP8 ? c.k_scale : 1.0f), FP8 ? c.v_scale : 1.0f);
+}
+
 template <int BS>
 hipError_t launch_prefill_bs(const KvDesc& c, const void* q, int32_t Hq, int32_t total_q,
                              const int32_t* cu_q, const int32_t* prior, const int32_t* tables,
                              int32_t B, int32_t max_blocks, int32_t max_chunk, float scale,
                              float* out, hipStream_t s) {
   const int32_t nqt = (max_chunk + kBq - 1) / kBq;
-  const float qk_scale = scale * kLog2e;
-  const int64_t pairs = static_cast<int64_t>(B) * Hq;
-  const dim3 grid(static_cast<uint32_t>((pairs + kXcds - 1) / kXcds * kXcds * nqt));
+#define PA_ARGS c, q, Hq, total_q, cu_q, prior, tables, B, max_blocks, nqt, scale, out, s
   if (c.head_dim == 128) {
-    prefill_kernel<128, BS><<<grid, dim3(kThreads), 0, s>>>(
-        static_cast<const half_t*>(q), static_cast<const half_t*>(c.k),
-        static_cast<const half_t*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
-        max_blocks, c.num_blocks, nqt, qk_scale);
+    if (c.fp8) run_prefill<128, BS, true>(PA_ARGS);
+    else run_prefill<128, BS, false>(PA_ARGS);
   } else {
-    prefill_kernel<64, BS><<<grid, dim3(kThreads), 0, s>>>(
-        static_cast<const half_t*>(q), static_cast<const half_t*>(c.k),
-        static_cast<const half_t*>(c.v), cu_q, prior, tables, out, B, Hq, c.num_kv_heads, total_q,
-        max_blocks, c.num_blocks, nqt, qk_scale);
+    if (c.fp8) run_prefill<64, BS, true>(PA_ARGS);
+    else run_prefill<64, BS, false>(PA_ARGS);
   }
+#undef PA_ARGS
   return hipGetLastError();
 }
 

@@ -53,12 +53,34 @@ __device__ __forceinline__ int kswz(int r) {
   else return swz8(r);
 }
 
-// Registers holding one K/V tile between its global loads and its LDS stores.
-template <int D>
+// Cache element: fp16, or an e4m3 code (widened to fp16 on the way to LDS).
+template <bool FP8>
+using elem_t = std::conditional_t<FP8, uint8_t, half_t>;
+
+// Registers holding one K/V tile between its global loads and its LDS stores,
+// in the cache's format: per K chunk 8 values, per V row quad 4 values.
+template <int D, bool FP8>
 struct Stage {
-  u32x4_t k[PGeom<D>::KLOADS];
-  u32x2_t v[8];   // keys 4 g + i of block 2 p (v[i]) and of block 2 p + 1 (v[4 + i])
+  using KReg = std::conditional_t<FP8, u32x2_t, u32x4_t>;
+  using VReg = std::conditional_t<FP8, uint32_t, u32x2_t>;
+  KReg k[PGeom<D>::KLOADS];
+  VReg v[8];   // keys 4 g + i of block 2 p (v[i]) and of block 2 p + 1 (v[4 + i])
 };
+
+// 8 K values (one 16-byte LDS chunk) and 4 V values as fp16.  Every e4m3
+// value is exact in fp16; the scales are applied to the scores and the output.
+__device__ __forceinline__ u32x4_t widen_k(const u32x4_t& k) { return k; }
+__device__ __forceinline__ u32x4_t widen_k(const u32x2_t& k) {
+  return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[1], 1.0f, true))};
+}
+__device__ __forceinline__ u32x2_t widen_v(const u32x2_t& v) { return v; }
+__device__ __forceinline__ u32x2_t widen_v(uint32_t v) {
+  return u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true))};
+}
 
 // Rank of lane b's sequence (b < B <= 64) by total length, longest first,
 // ties by index; lanes >= B get rank 64.
@@ -157,28 +179,30 @@ struct StageGeom {
 
 // Issue the global loads of a key tile.  Every load stays inside the pool;
 // rows past the context are fixed up by store_tile.
-template <int D, int BS>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D, BS>& sg, const TileBlocks& tb,
-                                          const half_t* __restrict__ kc,
-                                          const half_t* __restrict__ vc, int64_t blk_stride,
+template <int D, int BS, bool FP8>
+__device__ __forceinline__ void load_tile(Stage<D, FP8>& st, const StageGeom<D, BS>& sg,
+                                          const TileBlocks& tb, const elem_t<FP8>* __restrict__ kc,
+                                          const elem_t<FP8>* __restrict__ vc, int64_t blk_stride,
                                           int w) {
   using G = PGeom<D>;
+  using KReg = typename Stage<D, FP8>::KReg;
+  using VReg = typename Stage<D, FP8>::VReg;
 #pragma unroll
   for (int i = 0; i < G::KLOADS; ++i) {
     const int key = sg.k_row + i * (kThreads / G::CPR);
     const int blk = ((i * kThreads + 64 * w) / G::CPR) / BS;  // wave-uniform
-    const half_t* base = kc + static_cast<int64_t>(pick_block(blk, tb)) * blk_stride;
-    st.k[i] = *reinterpret_cast<const u32x4_t*>(base + sg.k_head + (key % BS) * D + sg.k_col * 8);
+    const elem_t<FP8>* base = kc + static_cast<int64_t>(pick_block(blk, tb)) * blk_stride;
+    st.k[i] = *reinterpret_cast<const KReg*>(base + sg.k_head + (key % BS) * D + sg.k_col * 8);
   }
   if (sg.v_on) {
     // pair p = w / 2 and group pair g / 2 = w % 2 are wave-uniform
     const int kb = 32 * (w >> 1) + 8 * (w & 1);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const half_t* base = vc + static_cast<int64_t>(pick_block((kb + 16 * hb) / BS, tb)) * blk_stride;
+      const elem_t<FP8>* base = vc + static_cast<int64_t>(pick_block((kb + 16 * hb) / BS, tb)) * blk_stride;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        st.v[4 * hb + i] = *reinterpret_cast<const u32x2_t*>(base + sg.v_off[hb] + i * D);
+        st.v[4 * hb + i] = *reinterpret_cast<const VReg*>(base + sg.v_off[hb] + i * D);
     }
   }
 }
@@ -187,21 +211,25 @@ __device__ __forceinline__ void load_tile(Stage<D>& st, const StageGeom<D, BS>& 
 // tile holding the end of the keys (tail), V rows at or past n_keys are zeroed
 // (their P is 0, but stale cache rows may hold non-finite bits); K rows there
 // only produce scores that the causal mask removes.
-template <int D, int BS>
-__device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D, BS>& sg, half_t* __restrict__ sK,
-                                           half_t* __restrict__ sVt, bool tail, int key0, int n_keys) {
+template <int D, int BS, bool FP8>
+__device__ __forceinline__ void store_tile(const Stage<D, FP8>& st, const StageGeom<D, BS>& sg,
+                                           half_t* __restrict__ sK, half_t* __restrict__ sVt, bool tail,
+                                           int key0, int n_keys) {
   using G = PGeom<D>;
 #pragma unroll
   for (int i = 0; i < G::KLOADS; ++i) {
     const int r = sg.k_row + i * (kThreads / G::CPR);
-    *reinterpret_cast<u32x4_t*>(&sK[r * D + ((sg.k_col ^ kswz<D>(r)) << 3)]) = st.k[i];
+    *reinterpret_cast<u32x4_t*>(&sK[r * D + ((sg.k_col ^ kswz<D>(r)) << 3)]) = widen_k(st.k[i]);
   }
   if (!sg.v_on) return;
+  u32x2_t v[8];
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) v[s8] = widen_v(st.v[s8]);
   if (tail) {
     const int kb = key0 + 32 * (sg.vq >> 2) + 4 * (sg.vq & 3);
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
-      if (kb + 16 * (s8 >> 2) + (s8 & 3) >= n_keys) st.v[s8] = u32x2_t{0u, 0u};
+      if (kb + 16 * (s8 >> 2) + (s8 & 3) >= n_keys) v[s8] = u32x2_t{0u, 0u};
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -210,20 +238,22 @@ __device__ __forceinline__ void store_tile(Stage<D>& st, const StageGeom<D, BS>&
     u32x4_t row;
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd)
-      row[wd] = __builtin_amdgcn_perm(st.v[2 * wd + 1][j >> 1], st.v[2 * wd][j >> 1], sel);
+      row[wd] = __builtin_amdgcn_perm(v[2 * wd + 1][j >> 1], v[2 * wd][j >> 1], sel);
     const int r = 4 * sg.dq + j;
     *reinterpret_cast<u32x4_t*>(&sVt[r * kBk + ((sg.vq ^ swz8(r)) << 3)]) = row;
   }
 }
 
-// grid (ceil(B * Hq / 8) * 8 * nqt), block 256.  qk_scale = softmax scale * log2 e.
-template <int D, int BS>
+// grid (ceil(B * Hq / 8) * 8 * nqt), block 256.  qk_scale = softmax scale *
+// log2 e (* k_scale for an e4m3 cache); v_scale multiplies the output (1 for
+// fp16).
+template <int D, int BS, bool FP8 = false>
 __device__ __forceinline__ void prefill_body(
-    int u, const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
-    const int32_t* __restrict__ tables, float* __restrict__ out, int32_t B, int32_t Hq,
-    int32_t Hkv, int32_t total_q, int32_t max_blocks, int32_t num_blocks, int32_t nqt,
-    float qk_scale) {
+    int u, const half_t* __restrict__ q, const elem_t<FP8>* __restrict__ kc,
+    const elem_t<FP8>* __restrict__ vc, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ prior, const int32_t* __restrict__ tables, float* __restrict__ out,
+    int32_t B, int32_t Hq, int32_t Hkv, int32_t total_q, int32_t max_blocks, int32_t num_blocks,
+    int32_t nqt, float qk_scale, float v_scale = 1.0f) {
   using G = PGeom<D>;
   __shared__ __attribute__((aligned(16))) half_t sK[2 * G::KBUF];
   __shared__ __attribute__((aligned(16))) half_t sVt[2 * G::VBUF];
@@ -301,10 +331,10 @@ __device__ __forceinline__ void prefill_body(
   StageGeom<D, BS> sg;
   sg.init(tid, kvh);
   const int64_t blk_stride = static_cast<int64_t>(Hkv) * BS * D;
-  Stage<D> stg;
+  Stage<D, FP8> stg;
   int ids_next = 0;
   if (ntiles > 0) {
-    load_tile<D, BS>(stg, sg, tile_blocks<BS>(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
+    load_tile<D, BS, FP8>(stg, sg, tile_blocks<BS>(trow, 0, max_blocks, num_blocks), kc, vc, blk_stride, w);
     ids_next = tile_ids_lanes<BS>(trow, 1, max_blocks, lane);
     store_tile<D, BS>(stg, sg, sK, sVt, kBk > n_keys, 0, n_keys);
   }
@@ -337,7 +367,7 @@ __device__ __forceinline__ void prefill_body(
     if (more) {
       const TileBlocks tb = tile_blocks_from<BS>(ids_next, num_blocks);
       ids_next = tile_ids_lanes<BS>(trow, kt + 2, max_blocks, lane);
-      load_tile<D, BS>(stg, sg, tb, kc, vc, blk_stride, w);
+      load_tile<D, BS, FP8>(stg, sg, tb, kc, vc, blk_stride, w);
     }
     __syncthreads();  // buffer PAR written; buffer 1 - PAR no longer read
 
@@ -451,7 +481,7 @@ __device__ __forceinline__ void prefill_body(
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     if (!qvalid[st]) continue;
-    const float inv = 1.0f / lt;
+    const float inv = v_scale / lt;
     float* orow = out + (static_cast<int64_t>(row0 + qrow[st]) * Hq + h) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < G::DT; ++dt) {
@@ -461,15 +491,15 @@ __device__ __forceinline__ void prefill_body(
 }
 
 
-template <int D, int BS>
+template <int D, int BS, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
-    const half_t* __restrict__ q, const half_t* __restrict__ kc, const half_t* __restrict__ vc,
+    const half_t* __restrict__ q, const elem_t<FP8>* __restrict__ kc, const elem_t<FP8>* __restrict__ vc,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ prior,
     const int32_t* __restrict__ tables, float* __restrict__ out, int32_t B, int32_t Hq,
     int32_t Hkv, int32_t total_q, int32_t max_blocks, int32_t num_blocks, int32_t nqt,
-    float qk_scale) {
-  prefill_body<D, BS>(blockIdx.x, q, kc, vc, cu_q, prior, tables, out, B, Hq, Hkv, total_q, max_blocks,
-                  num_blocks, nqt, qk_scale);
+    float qk_scale, float v_scale) {
+  prefill_body<D, BS, FP8>(blockIdx.x, q, kc, vc, cu_q, prior, tables, out, B, Hq, Hkv, total_q,
+                           max_blocks, num_blocks, nqt, qk_scale, v_scale);
 }
 
 }  // namespace

@@ -134,13 +134,17 @@ class PrefillCase:
     """Library-side state of one chunked-prefill workload: prior context and
     chunk written through the allocator, outputs poisoned with NaN."""
 
-    def __init__(self, w, block_size: int = 16):
+    def __init__(self, w, block_size: int = 16, fp8: bool = False):
         self.w = w
         self.bs = block_size
+        self.fp8 = fp8
+        self.scales = fp8_scales(w, range(w.batch)) if fp8 else None
+        ks, vs = self.scales if fp8 else (1.0, 1.0)
         nb, order = pool_geometry(w, block_size)
         self.pool = pa.pa_pool_create(nb, block_size, order)
-        self.cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size,
-                                fill=float("nan"))
+        self.cache = pa.KvCache(nb, w.num_kv_heads, w.head_dim, block_size=block_size, fp8=fp8,
+                                k_scale=ks, v_scale=vs, fill=(255 if fp8 else float("nan")))
+        self._kv = {}
         self.ids = []
         for b in range(w.batch):
             s = pa.pa_seq_create(self.pool)
@@ -171,9 +175,20 @@ class PrefillCase:
         torch.cuda.synchronize()
         return self.out.cpu().numpy()
 
+    def kv(self, b):
+        """Sequence b's K/V as the cache holds them (dequantised for e4m3)."""
+        if b not in self._kv:
+            k, v = self.w.kv(b, cache=True)
+            if self.fp8:
+                ks, vs = self.scales
+                k = e4m3_dequantize(e4m3_quantize(k, ks), ks)
+                v = e4m3_dequantize(e4m3_quantize(v, vs), vs)
+            self._kv[b] = (k, v)
+        return self._kv[b]
+
     def ref_row(self, b, i, h, scale=None):
         w = self.w
-        k, v = w.kv(b, cache=True)
+        k, v = self.kv(b)
         kh = h // (w.num_heads // w.num_kv_heads)
         n = int(w.prior[b]) + i + 1
         r = int(self.cu_np[b]) + i
@@ -184,13 +199,18 @@ class Mixed:
     """One cache holding a prefill batch (prior context + chunk) and a decode
     batch, with the argument dictionaries of pa_mixed_step for both halves."""
 
-    def __init__(self, wp, wd, block_size: int = 16):
+    def __init__(self, wp, wd, block_size: int = 16, fp8: bool = False):
         assert (wp.num_heads, wp.num_kv_heads, wp.head_dim) == (wd.num_heads, wd.num_kv_heads, wd.head_dim)
         self.wp, self.wd = wp, wd
+        self.fp8 = fp8
+        if fp8:  # one scale per tensor over both batches: the larger of the two
+            (kp, vp), (kd, vd) = fp8_scales(wp, range(wp.batch)), fp8_scales(wd, range(wd.batch))
+            self.scales = (max(kp, kd), max(vp, vd))
+        ks, vs = self.scales if fp8 else (1.0, 1.0)
         n = pool_geometry(wp, block_size)[0] + pool_geometry(wd, block_size)[0]
         self.pool = pa.pa_pool_create(n, block_size)
-        self.cache = pa.KvCache(n, wp.num_kv_heads, wp.head_dim, block_size=block_size,
-                                fill=float("nan"))
+        self.cache = pa.KvCache(n, wp.num_kv_heads, wp.head_dim, block_size=block_size, fp8=fp8,
+                                k_scale=ks, v_scale=vs, fill=(255 if fp8 else float("nan")))
         self.pids = []
         for b in range(wp.batch):
             s = pa.pa_seq_create(self.pool)
@@ -250,6 +270,10 @@ class Mixed:
         wp, wd = self.wp, self.wd
         for b in range(wp.batch):
             k, v = wp.kv(b, cache=True)
+            if self.fp8:
+                ks, vs = self.scales
+                k = e4m3_dequantize(e4m3_quantize(k, ks), ks)
+                v = e4m3_dequantize(e4m3_quantize(v, vs), vs)
             C = int(wp.chunk[b])
             rows = range(C) if rows_per_seq is None else sorted({0, C - 1, C // 2} & set(range(C)))
             for i in rows:
@@ -258,5 +282,6 @@ class Mixed:
                 for h in range(wp.num_heads):
                     kh = h // (wp.num_heads // wp.num_kv_heads)
                     close(outp[r, h], attention_fp64(wp.q[r, h], k[:n, kh], v[:n, kh], wp.scale))
-        ref = oracle_decode(wd, [(i, h) for i in range(wd.batch) for h in range(wd.num_heads)])
+        ref = oracle_decode(wd, [(i, h) for i in range(wd.batch) for h in range(wd.num_heads)], None,
+                            self.scales if self.fp8 else None)
         close(outd, np.array([[ref[(i, h)] for h in range(wd.num_heads)] for i in range(wd.batch)]))

@@ -92,9 +92,14 @@ def test_device_entry_points_reject_bad_arguments_without_touching_a_gpu():
     # workspace too small
     st = pa.lib.pa_decode(ctypes.byref(d5), 16, 2, 16, 16, None, 1, 4, 4096, 1.0, 16, None, 0, None)
     assert st == pa.PA_ERR_BAD_ARG and b"workspace" in pa.lib.pa_last_error()
-    st = pa.lib.pa_prefill_chunk(ctypes.byref(pa.pa_kv_cache(16, 16, 4, 16, 1, 128, 1, 1.0, 1.0)),
+    # e4m3 prefill is supported, but not with a 512-byte (8 x 64) tile
+    st = pa.lib.pa_prefill_chunk(ctypes.byref(pa.pa_kv_cache(16, 16, 4, 8, 1, 64, 1, 1.0, 1.0)),
                                  16, 1, 4, 16, 16, 16, 1, 4, 4, 1.0, 16, None)
     assert st == pa.PA_ERR_UNSUPPORTED
+    # the appending decode checks its new rows before anything else runs
+    st = pa.lib.pa_decode_append(ctypes.byref(d5), 16, 2, None, None, 16, 16, None, 1, 4, 16, 1.0, 16,
+                                 16, 1 << 20, None, 0, None)
+    assert st == pa.PA_ERR_BAD_ARG and b"k_new" in pa.lib.pa_last_error()
 
 
 def test_workspace_size_formula():

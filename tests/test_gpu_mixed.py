@@ -48,3 +48,18 @@ def test_mixed_step_with_one_part_empty():
     pa.pa_mixed_step(m.cache, wp.scale, None, m.decode)
     torch.cuda.synchronize()
     m.check_oracle(m.prefill["out"].cpu().numpy(), m.decode["out"].cpu().numpy())
+
+
+@pytest.mark.parametrize("dlens", [[1, 0, 37, 300, 1600], [20000, 70]])
+def test_mixed_step_fp8_cache(dlens):
+    """An e4m3 cache: the prefill half equals pa_prefill_chunk bit for bit,
+    the decode half matches pa_decode, both match the oracle over the
+    dequantised cache (20000 tokens: the two-launch form)."""
+    wp = workloads.custom_prefill(181, [0, 37, 300], [1, 130, 200], 4, 2, 128)
+    wd = workloads.custom_decode(182, dlens, 4, 2, 128)
+    m = Mixed(wp, wd, fp8=True)
+    outp, outd = m.run_mixed(wp.scale)
+    sp, sd = m.run_separate(wp.scale)
+    assert np.array_equal(outp, sp)
+    close(outd, sd.astype(np.float64))
+    m.check_oracle(outp, outd)

@@ -88,3 +88,29 @@ def test_two_half_chunks_equal_one_chunk():
     close(np.concatenate(halves).astype(np.float64), one.astype(np.float64))
     for i in (0, 255, 256, 511):
         close(one[i, 2], case.ref_row(0, i, 2))
+
+
+@pytest.mark.parametrize("block_size", [8, 16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_cache_prefill(block_size, D):
+    """Chunked prefill over an e4m3 cache: the kernel's own error is held to
+    the fp16 bound against the oracle over the dequantised cache."""
+    if D * block_size < 1024:
+        pytest.skip("an e4m3 tile below 1 KiB is refused (covered by the ABI test)")
+    w = workloads.custom_prefill(401 + D + block_size, [0, 37, 300, 16, 900], [1, 21, 200, 129, 64],
+                                 4, 2, D)
+    check_all(PrefillCase(w, block_size=block_size, fp8=True))
+
+
+def test_fp8_cache_prefill_full_size_sampled():
+    """The 8 x 512-row workload over an e4m3 cache, sampled rows."""
+    w = workloads.chunked_prefill()
+    case = PrefillCase(w, fp8=True)
+    got = case.run()
+    rng = np.random.default_rng(17)
+    for b in range(w.batch):
+        for i in (0, 255, 511):
+            r = int(case.cu_np[b]) + i
+            for h in rng.integers(0, w.num_heads, 2):
+                close(got[r, h], case.ref_row(b, i, int(h)))
+    assert np.isfinite(got).all()

@@ -136,6 +136,22 @@ pa_status pa_seq_create(pa_pool *pool, int32_t *seq_out);
 pa_status pa_alloc_append(pa_pool *pool, int32_t seq, int32_t n_tokens,
                           int32_t *slots_out, int32_t *cow_out);
 
+/* One decode step's reservations in one call: pa_alloc_append (or, with
+ * token_ids, pa_append_tokens) for seqs[0], seqs[1], ... in that order, with
+ * n_tokens[i] tokens for seqs[i] (the pages' per-sequence lifecycle, [p2]
+ * "Deep dive", batched so a step of B sequences costs one call).  All or
+ * nothing: the status is that of the first call of the sequence that would
+ * fail, and then the pool is unchanged.  slots_out: sum(n_tokens) entries in
+ * batch order.  cow_out: 2 * n_seqs entries, {src, dst} or {-1, -1} per
+ * sequence (a later sequence sharing the same partly filled block with an
+ * earlier one may find it no longer shared, exactly as with single calls).
+ * token_ids: NULL, or sum(n_tokens) ids back to back.  Each sequence may appear
+ * once.  Errors: BAD_ARG (NULL arrays, negative count, a repeated or swapped-out
+ * sequence), BAD_SEQ, NO_BLOCKS, CAPACITY. */
+pa_status pa_alloc_append_batch(pa_pool *pool, const int32_t *seqs, int32_t n_seqs,
+                                const int32_t *n_tokens, const int32_t *token_ids,
+                                int32_t *slots_out, int32_t *cow_out);
+
 /* pa_alloc_append that also records the new tokens' ids, so that the blocks
  * they fill can enter the prefix cache (pa_cache_commit).  A sequence's ids are
  * known only while every append supplied them: after a pa_alloc_append its later

@@ -87,6 +87,8 @@ _SIGNATURES = {
     "pa_seq_create": (ctypes.c_int32, [ctypes.c_void_p, _i32p]),
     "pa_alloc_append": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
     "pa_append_tokens": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
+    "pa_alloc_append_batch": (ctypes.c_int32, [ctypes.c_void_p, _i32p, ctypes.c_int32, _i32p, _i32p, _i32p,
+                                               _i32p]),
     "pa_alloc_prompt": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i32p]),
     "pa_cache_commit": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, _i32p]),
     "pa_swap_space": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
@@ -208,6 +210,26 @@ def pa_append_tokens(pool: Pool, seq: int, tokens) -> Tuple[np.ndarray, Optional
     cow = np.full(2, -1, dtype=np.int32)
     _check(lib.pa_append_tokens(pool.handle, seq, _p(t) if len(t) else None, len(t), _p(slots), _p(cow)))
     return slots, (None if cow[0] < 0 else (int(cow[0]), int(cow[1])))
+
+
+def pa_alloc_append_batch(pool: Pool, seqs, n_tokens, token_ids=None) -> Tuple[np.ndarray, np.ndarray]:
+    """One call for many sequences (in order, all or nothing).  Returns (slots
+    int32[sum(n_tokens)] in batch order, cow int32[len(seqs)][2] with -1 rows
+    where no copy-on-write happened)."""
+    s = _i32(seqs)
+    n = _i32(n_tokens)
+    if len(s) != len(n):
+        raise PaError(PA_ERR_BAD_ARG, "seqs and n_tokens differ in length")
+    total = int(n.sum()) if len(n) else 0
+    t = None if token_ids is None else _i32(token_ids)
+    if t is not None and len(t) != total:
+        raise PaError(PA_ERR_BAD_ARG, "token_ids must hold sum(n_tokens) ids")
+    slots = np.empty(max(total, 1), dtype=np.int32)
+    cow = np.full((max(len(s), 1), 2), -1, dtype=np.int32)
+    _check(lib.pa_alloc_append_batch(pool.handle, _p(s) if len(s) else None, len(s),
+                                     _p(n) if len(n) else None,
+                                     _p(t) if t is not None and len(t) else None, _p(slots), _p(cow)))
+    return slots[:total], cow[:len(s)]
 
 
 def pa_alloc_prompt(pool: Pool, seq: int, tokens) -> Tuple[np.ndarray, int]:

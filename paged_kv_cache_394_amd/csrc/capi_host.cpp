@@ -81,6 +81,17 @@ pa_status pa_append_tokens(pa_pool* pool, int32_t seq, const int32_t* tokens, in
   return pa::ok();
 }
 
+pa_status pa_alloc_append_batch(pa_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                                const int32_t* n_tokens, const int32_t* token_ids, int32_t* slots_out,
+                                int32_t* cow_out) {
+  if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_alloc_append_batch: pool is NULL");
+  std::string err;
+  const pa::Status st =
+      pool->impl->alloc_append_batch(seqs, n_seqs, n_tokens, token_ids, slots_out, cow_out, &err);
+  if (st != pa::kOk) return fail(st, err);
+  return pa::ok();
+}
+
 pa_status pa_alloc_prompt(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
                           int32_t* slots_out, int32_t* hit_tokens_out) {
   if (pool == nullptr) return fail(PA_ERR_BAD_ARG, "pa_alloc_prompt: pool is NULL");

@@ -1,6 +1,8 @@
 // Host block manager; see pool.hpp for the model and its sources.
 #include "pool.hpp"
 
+#include <unordered_map>
+
 #include <cstring>
 #include <new>
 
@@ -197,6 +199,77 @@ Status BlockPool::alloc_append(int32_t seq, int32_t n, const int32_t* tokens, in
   tokens_ += n;
   waste_ += (blocks_after * bs_ - s.len) - waste_before;
   if (record) s.tokens.insert(s.tokens.end(), tokens, tokens + n);
+  return kOk;
+}
+
+Status BlockPool::alloc_append_batch(const int32_t* seqs, int32_t n_seqs, const int32_t* counts,
+                                     const int32_t* tokens, int32_t* slots, int32_t* cow,
+                                     std::string* err) {
+  if (n_seqs < 0 || (n_seqs > 0 && (seqs == nullptr || counts == nullptr || cow == nullptr))) {
+    *err = "pa_alloc_append_batch: bad arguments";
+    return kBadArg;
+  }
+  // Dry run in batch order: the checks of each single call, with the blocks
+  // earlier calls take and the references their copies drop.
+  int64_t total = 0, need = 0;
+  std::unordered_map<int32_t, int32_t> dropped;  // shared last block -> references given up
+  std::unordered_map<int32_t, char> seen;
+  try {
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      const int32_t sid = seqs[i], n = counts[i];
+      if (!live(sid)) {
+        *err = "pa_alloc_append_batch: unknown sequence";
+        return kBadSeq;
+      }
+      const Seq& s = seqs_[sid];
+      if (n < 0 || s.swapped || !seen.emplace(sid, 1).second) {
+        *err = "pa_alloc_append_batch: negative count, swapped-out or repeated sequence";
+        return kBadArg;
+      }
+      total += n;
+      if (n == 0) continue;
+      const int64_t blocks_after = ceil_div(s.len + n, bs_);
+      if (blocks_after * bs_ >= (int64_t(1) << 31)) {
+        *err = "pa_alloc_append_batch: sequence would exceed 2^31 tokens";
+        return kBadArg;
+      }
+      need += blocks_after - static_cast<int64_t>(s.table.size());
+      if (s.len % bs_ != 0) {
+        const int32_t last = s.table.back();
+        int32_t& d = dropped[last];
+        if (ref_[last] - d > 1) {  // still shared when this call runs: it copies
+          ++need;
+          ++d;
+        }
+      }
+      if (need > nfree_) {
+        *err = "pa_alloc_append_batch: not enough free blocks";
+        return kNoBlocks;
+      }
+    }
+    if (total > 0 && slots == nullptr) {
+      *err = "pa_alloc_append_batch: slots_out is NULL";
+      return kBadArg;
+    }
+    // the only other failure of the single calls, a host allocation, happens here
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      Seq& s = seqs_[seqs[i]];
+      s.table.reserve(static_cast<size_t>(ceil_div(s.len + counts[i], bs_)));
+      if (tokens != nullptr && static_cast<int64_t>(s.tokens.size()) == s.len)
+        s.tokens.reserve(static_cast<size_t>(s.len + counts[i]));
+    }
+  } catch (const std::bad_alloc&) {
+    *err = "pa_alloc_append_batch: out of host memory";
+    return kCapacity;
+  }
+  // --- no failure past this point ---
+  int64_t off = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const Status st = alloc_append(seqs[i], counts[i], tokens != nullptr ? tokens + off : nullptr,
+                                   slots + off, cow + 2 * i, err);
+    (void)st;  // kOk: every condition was checked above
+    off += counts[i];
+  }
   return kOk;
 }
 

@@ -59,6 +59,13 @@ class BlockPool {
   // blocks are then never cached).
   Status alloc_append(int32_t seq, int32_t n, const int32_t* tokens, int32_t* slots, int32_t* cow,
                       std::string* err);
+  // alloc_append for seqs[0], seqs[1], ... in that order (counts[i] tokens
+  // each; tokens: their ids back to back, or nullptr), all or nothing: the
+  // first call that would fail decides the status and nothing is changed.
+  // slots: sum(counts) entries in batch order; cow: 2 entries per sequence.
+  // A sequence may appear once.
+  Status alloc_append_batch(const int32_t* seqs, int32_t n_seqs, const int32_t* counts,
+                            const int32_t* tokens, int32_t* slots, int32_t* cow, std::string* err);
   // Admit a prompt into an empty sequence, reusing cached full blocks; slots
   // gets the slots of tokens hit..n-1; at most (n - 1) / block_size blocks are
   // reused (the last token is always computed).

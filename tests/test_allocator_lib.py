@@ -2,6 +2,7 @@
 tables, lengths, slots, copy-on-write pairs, reference counts, free-queue order
 and counters after every operation.  Host logic only; no GPU."""
 
+import copy
 import random
 
 import numpy as np
@@ -57,6 +58,40 @@ class Pair:
         if st_ == Status.OK:
             assert slots.tolist() == oslots and cow == ocow
         return st_, slots, cow
+
+    def append_batch(self, seqs, counts, token_ids=None):
+        """The library's batched call against single oracle calls in batch
+        order, all or nothing: on the first failure the oracle is restored and
+        that call's status is expected (a repeated sequence is BAD_ARG)."""
+        try:
+            slots, cow = pa.pa_alloc_append_batch(self.lib, seqs, counts, token_ids)
+            lib_st = Status.OK
+        except pa.PaError as e:
+            lib_st, slots, cow = e.name, None, None
+        snapshot = copy.deepcopy(self.orc)
+        want_st, oslots, ocow, off, seen = Status.OK, [], [], 0, set()
+        for sid, n in zip(seqs, counts):
+            if sid in seen and sid in self.orc.tables:
+                want_st = Status.BAD_ARG
+                break
+            seen.add(sid)
+            if token_ids is None:
+                st_, sl, cw = self.orc.alloc_append(sid, n)
+            else:
+                st_, sl, cw = self.orc.append_tokens(sid, list(token_ids[off:off + max(n, 0)]))
+            if st_ != Status.OK:
+                want_st = st_
+                break
+            oslots += sl
+            ocow.append(cw if cw else (-1, -1))
+            off += n
+        if want_st != Status.OK:
+            self.orc = snapshot
+        assert lib_st == want_st
+        if want_st == Status.OK:
+            assert slots.tolist() == oslots
+            assert [tuple(x) for x in cow.tolist()] == [tuple(c) for c in ocow]
+        return want_st
 
     def prompt(self, s, toks):
         try:
@@ -227,7 +262,7 @@ def test_errors_leave_state_unchanged():
         pa.pa_pool_create(1 << 28, 16)
 
 
-ops = st.lists(st.tuples(st.sampled_from(["new", "append", "append1", "fork", "free", "badfree"]),
+ops = st.lists(st.tuples(st.sampled_from(["new", "append", "append1", "fork", "free", "badfree", "batch"]),
                          st.integers(0, 50), st.integers(0, 70)), min_size=1, max_size=80)
 
 
@@ -249,6 +284,16 @@ def test_random_op_sequences_match_oracle(ops, n, bs, seed):
             live.append(p.fork(live[i % len(live)]))
         elif op == "free":
             p.free(live.pop(i % len(live)))
+        elif op == "batch":
+            # a decode step over a slice of the live sequences (sometimes with a
+            # repeat or an unknown id), k tokens for the first and 1 for the rest
+            r = random.Random(seed * 1000 + i + k)
+            pick = r.sample(live, r.randint(0, len(live)))
+            if pick and r.random() < 0.1:
+                pick.append(pick[0])
+            if r.random() < 0.05:
+                pick.append(1000 + i)
+            p.append_batch(pick, [k % 5 if j == 0 else 1 for j in range(len(pick))])
         else:
             p.free(1000 + i)
         p.check()
@@ -358,3 +403,40 @@ def test_swap_ops_match_oracle(ops, n, host, bs, seed):
         else:
             p.swap(live[i % len(live)], op == "out")
         p.check()
+
+
+def test_batched_append_copy_on_write_and_all_or_nothing():
+    """Two forks sharing a partly filled block: in one batch the first copies
+    it and the second then owns the original, as with single calls; a batch
+    that runs out of blocks part-way changes nothing."""
+    p = Pair(12, 16)
+    a = p.create()
+    p.append(a, 20)                       # blocks: 1 full + 1 partial
+    b = p.fork(a)
+    c = p.fork(a)                         # the partial block is held three times
+    assert p.append_batch([b, c, a], [1, 1, 1]) == Status.OK
+    p.check()
+    _, _, ref = pa.pa_pool_state(p.lib)
+    # b and c copied the block; a appended into the original, now its own
+    tabs = {s: pa.pa_seq_table(p.lib, s)[0].tolist() for s in (a, b, c)}
+    assert len({tabs[a][1], tabs[b][1], tabs[c][1]}) == 3 and ref[tabs[a][1]] == 1
+    stats_before, free_before, _ = pa.pa_pool_state(p.lib)
+    # 12 blocks: 2 + 1 + 1 used; asking 3 x 64 tokens needs 4 + 3 + 3 more
+    assert p.append_batch([a, b, c], [64, 64, 64]) == Status.NO_BLOCKS
+    p.check()
+    assert pa.pa_pool_state(p.lib)[:2] == (stats_before, free_before)
+    assert p.append_batch([a, a], [1, 1]) == Status.BAD_ARG
+    assert p.append_batch([a, 99], [1, 1]) == Status.BAD_SEQ
+    assert p.append_batch([], []) == Status.OK
+    p.check()
+
+
+def test_batched_append_with_token_ids_feeds_the_prefix_cache():
+    p = Pair(16, 4)
+    s = [p.create() for _ in range(3)]
+    assert p.append_batch(s, [5, 7, 4], list(range(16))) == Status.OK
+    for x in s:
+        p.commit(x)
+    p.check()
+    stats, _, _ = pa.pa_pool_state(p.lib)
+    assert stats["cached_blocks"] == 1 + 1 + 1   # the full blocks of 5, 7 and 4 tokens

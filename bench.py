@@ -638,6 +638,76 @@ The write_kv and copyBuffer rows are dominated by the set-up writes of whole con
     print(body)
 
 
+PREFILL_PMC_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE",
+)
+
+
+def summarize_prefill_pmc(dir1, dir2, out_md):
+    """Counter summary of the 8 x 512-row chunked prefill (prefill_kernel<128,
+    16, fp16>) from two rocprofv3 --pmc runs of --prefill-only."""
+    def latest(d):
+        hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not hits:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        return max(hits, key=os.path.getmtime)
+
+    vals = {}
+    for d, names in zip((dir1, dir2), PREFILL_PMC_PASSES):
+        path = latest(d)
+        for c in names.split():
+            table = _read_counter_csv(path, c)
+            keys = [k for k in table if "prefill_kernel" in k and "ILi128ELi16ELb0E" in k]
+            if not keys:
+                raise SystemExit(f"no fp16 prefill dispatch with {c} in {path}")
+            v = table[keys[0]]
+            vals[c] = sum(v) / len(v)
+    simds, xcds = 1024, 8
+    grbm = vals["GRBM_GUI_ACTIVE"] / xcds          # the counter sums the 8 XCDs
+    mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"]
+    wave = vals["SQ_WAVE_CYCLES"]
+    rows = [
+        ("kernel duration (GRBM_GUI_ACTIVE per XCD)", f"{grbm:,.0f} cycles"),
+        ("MFMA busy / (duration x 1024 SIMDs)", f"{mfma_busy / (grbm * simds):.3f}"),
+        ("MFMA instructions per dispatch", f"{vals['SQ_INSTS_MFMA']:,.0f}"),
+        ("SQ_INSTS_VALU / SQ_INSTS_MFMA", f"{vals['SQ_INSTS_VALU'] / vals['SQ_INSTS_MFMA']:.2f}"),
+        ("of which transcendental (exp2) per MFMA", f"{vals['SQ_INSTS_VALU_TRANS_F32'] / vals['SQ_INSTS_MFMA']:.2f}"),
+        ("SALU / LDS instructions per MFMA",
+         f"{vals['SQ_INSTS_SALU'] / vals['SQ_INSTS_MFMA']:.2f} / {vals['SQ_INSTS_LDS'] / vals['SQ_INSTS_MFMA']:.2f}"),
+        ("VALU and MFMA co-issue cycles / MFMA busy cycles",
+         f"{vals['SQ_VALU_MFMA_COEXEC_CYCLES'] / mfma_busy:.3f}"),
+        ("wave time issuing any instruction (ACTIVE_INST_ANY / WAVE_CYCLES)", f"{vals['SQ_ACTIVE_INST_ANY'] / wave:.3f}"),
+        ("wave time waiting on s_waitcnt (WAIT_ANY / WAVE_CYCLES)", f"{vals['SQ_WAIT_ANY'] / wave:.3f}"),
+        ("wave time waiting to issue (WAIT_INST_ANY / WAVE_CYCLES)", f"{vals['SQ_WAIT_INST_ANY'] / wave:.3f}"),
+        ("LDS bank conflicts per LDS instruction", f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_INSTS_LDS']:.3f}"),
+    ]
+    body = f"""# Chunked-prefill counters: prefill_kernel<128, 16, fp16>, 8 x 512-row chunks over 0..4096 cached tokens
+
+Commands (repository root, GPU box; one pass per counter set):
+
+    rocprofv3 --pmc {PREFILL_PMC_PASSES[0]} --output-format csv -d gpurun_out/pf_pmc1 -- python bench.py --prefill-only
+    rocprofv3 --pmc {PREFILL_PMC_PASSES[1]} --output-format csv -d gpurun_out/pf_pmc2 -- python bench.py --prefill-only
+    python bench.py --summarize-prefill-pmc gpurun_out/pf_pmc1 gpurun_out/pf_pmc2 {out_md}
+
+Averages over every dispatch of the kernel in the run (settle, warm-up and timed calls).  The
+SQ counters sum over all SIMDs; GRBM_GUI_ACTIVE sums the 8 XCDs.
+
+| quantity | value |
+|---|---|
+"""
+    for k, v in rows:
+        body += f"| {k} | {v} |\n"
+    body += "\nRaw per-dispatch averages:\n\n"
+    for k in sorted(vals):
+        body += f"- {k}: {vals[k]:,.0f}\n"
+    with open(out_md, "w") as f:
+        f.write(body)
+    print(body)
+
+
 def summarize_pmc(fetch_dir, write_dir):
     """Write the traffic summary from two rocprofv3 --pmc runs of --pmc-run."""
     def find(d):
@@ -703,12 +773,16 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="the chunked-prefill leg only (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "BENCH_LOG", "OUT_MD"))
+    ap.add_argument("--summarize-prefill-pmc", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "OUT_MD"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_prefill_pmc:
+        summarize_prefill_pmc(*args.summarize_prefill_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library runs on a single MI355X and has no "

@@ -363,6 +363,9 @@ def pa_write_kv(cache: KvCache, k_new: torch.Tensor, v_new: torch.Tensor, slots:
     """k_new/v_new [T][Hkv][D] float16, slots int32[T] on the device, cow_pairs
     host [(src, dst), ...] from pa_alloc_append."""
     T = int(slots.numel())
+    if T:
+        _shape(k_new, (T, cache.num_kv_heads, cache.head_dim), "pa_write_kv k_new")
+        _shape(v_new, (T, cache.num_kv_heads, cache.head_dim), "pa_write_kv v_new")
     pairs = _i32(cow_pairs if cow_pairs is not None else np.zeros((0, 2))).reshape(-1, 2)
     _check(lib.pa_write_kv(ctypes.byref(cache.desc), _dev(k_new, torch.float16) if T else None,
                            _dev(v_new, torch.float16) if T else None,
@@ -374,6 +377,23 @@ def pa_decode_workspace_bytes(B: int, num_heads: int, head_dim: int, max_context
     return int(lib.pa_decode_workspace_bytes(B, num_heads, head_dim, max_context_len))
 
 
+def _shape(t: torch.Tensor, shape, what: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _decode_shapes(cache: "KvCache", q, tables, lens, out, cached_blocks, what: str) -> None:
+    B, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: q head_dim {D} != cache head_dim {cache.head_dim}")
+    if tables.dim() != 2 or tables.shape[0] != B:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: tables must be [B][max_blocks]")
+    _shape(lens, (B,), f"{what} lens")
+    _shape(out, (B, Hq, D), f"{what} out")
+    if cached_blocks is not None:
+        _shape(cached_blocks, (B,), f"{what} cached_blocks")
+
+
 def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch.Tensor,
               max_context_len: int, scale: float, out: torch.Tensor,
               workspace: Optional[torch.Tensor] = None, stream=None,
@@ -382,6 +402,7 @@ def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch
     out float32 [B][Hq][D], workspace a device byte tensor, cached_blocks None or
     device int32[B] (from pa_shared_prefix; a read hint, not an input)."""
     B, Hq, D = q.shape
+    _decode_shapes(cache, q, tables, lens, out, cached_blocks, "pa_decode")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     cb = None if cached_blocks is None else _dev(cached_blocks, torch.int32)
     _check(lib.pa_decode(ctypes.byref(cache.desc), _dev(q, torch.float16), Hq,
@@ -400,6 +421,9 @@ def pa_decode_append(cache: KvCache, q: torch.Tensor, k_new: torch.Tensor, v_new
     context ending with it.  Other arguments as pa_decode; cow_pairs as
     pa_write_kv."""
     B, Hq, D = q.shape
+    _decode_shapes(cache, q, tables, lens, out, cached_blocks, "pa_decode_append")
+    _shape(k_new, (B, cache.num_kv_heads, D), "pa_decode_append k_new")
+    _shape(v_new, (B, cache.num_kv_heads, D), "pa_decode_append v_new")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     cb = None if cached_blocks is None else _dev(cached_blocks, torch.int32)
     pairs = _i32(cow_pairs if cow_pairs is not None else np.zeros((0, 2))).reshape(-1, 2)

@@ -14,7 +14,10 @@ kernel's average launch duration.
 Reported on one JSON line:
   value        KV-read GB/s of the step: algorithmic K+V bytes / step time
   roofline     the step kernel against 8 TB/s (algorithmic bytes / event time)
+  cold_step    the step with 512 MiB of unrelated writes before each step
+               (caches cold), an event pair per step: median, p10, p90
   ceiling      a plain device copy of 1 GiB (read + write GB/s), for context
+  read_ceiling torch's fastest read-bound reduction over 1 GiB, for context
   fp8_decode   the same batch with an e4m3 cache
   prefix_cow   32 sequences sharing an 800-token prompt: GB/s on unique and on
                logical K/V bytes
@@ -28,7 +31,9 @@ Reported on one JSON line:
                causal-valid FLOPs / time against the 2.5 PFLOP/s fp16 MFMA peak
   host         block-manager call times (admission per sequence, the step's
                batched reservation for all 64 sequences, table export)
-  cpu_baseline the float64 oracle on a bounded sample of the batch (host cores)
+  cpu_baseline the float64 oracle on a bounded sample of the batch (one core)
+  cpu_baseline_pool  the same oracle over the whole batch in a pool of
+               single-threaded processes (one per host core, 16 at most)
 
 Every leg first runs its own work untimed for SETTLE_S seconds, so that the
 GPU is at its steady clock when the W warm-up steps and the timed region
@@ -273,6 +278,46 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=20):
     del src, dst
     return {"kind": "torch.neg over 1 GiB fp16 (read 1 GiB + write 1 GiB)",
             "gbs_read_plus_write": round(2 * nbytes / (mean * 1e-3) / 1e9, 1), "ms": round(mean, 4)}
+
+
+def read_ceiling(torch, nbytes=1 << 30, reps=20):
+    """A read-bound device kernel for context: torch's row sums over 1 GiB of
+    fp16 laid out as 8192 rows of 65536 (reads 1 GiB, writes 16 KiB).  Of the
+    torch reductions and products over this buffer it is the fastest reader
+    on this part; a full-length sum reaches only about 60% of its rate."""
+    src = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda").view(-1, 65536)
+    acc = torch.empty(src.shape[0], dtype=torch.float16, device="cuda")
+    mean = time_events(torch, lambda: torch.sum(src, dim=1, out=acc), reps)
+    del src, acc
+    return {"kind": "torch.sum over rows of a 1 GiB fp16 matrix (8192 x 65536): read 1 GiB",
+            "gbs_read": round(nbytes / (mean * 1e-3) / 1e9, 1), "ms": round(mean, 4)}
+
+
+def cold_step(pa, torch, np, w, d, reps=30):
+    """The decode step with the caches flushed before every step: 512 MiB of
+    unrelated writes (twice the 256 MB last-level cache) between steps, and an
+    event pair around each step launch alone.  Per-launch event pairs read
+    about 2 us long on this part, so this is a conservative figure."""
+    junk = torch.empty(1 << 28, dtype=torch.float16, device="cuda")   # 512 MiB
+    settle(torch, lambda: append_call(pa, w, d))
+    ms = []
+    for _ in range(reps):
+        junk.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        append_call(pa, w, d)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del junk
+    ms = np.sort(np.array(ms))
+    kv, alg = decode_bytes(w, 2, fused=True)
+    med = float(np.median(ms))
+    return {"step_ms_median": round(med, 5), "step_ms_p10": round(float(ms[len(ms) // 10]), 5),
+            "step_ms_p90": round(float(ms[(9 * len(ms)) // 10]), 5),
+            "kv_gbs_median": round(kv / (med * 1e-3) / 1e9, 2),
+            "hbm_frac_median": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "flush": "512 MiB fill between steps"}
 
 
 def bench_prefix(pa, torch, np, workloads, reps):
@@ -523,6 +568,55 @@ def bench_block_sizes(pa, torch, np, workloads, w, steps, warmup, at16):
                         "waste_frac": round(1.0 - int(w.lens.sum()) / (blocks * bs), 5),
                         "prefill_ms": round(p_ms, 4)}
     return {"workload": "llama13b_decode (64 seqs, fp16) and chunked_prefill (8 x 512 rows)", **res}
+
+
+def _oracle_warm(_):
+    """Worker start-up of cpu_baseline_pool, kept out of its timed region."""
+    import oracle  # noqa: F401
+    import workloads
+    workloads.llama13b_decode()
+    return os.getpid()
+
+
+def _oracle_seqs(bs):
+    """Worker of cpu_baseline_pool: the oracle for sequences bs of the batch."""
+    from threadpoolctl import threadpool_limits
+    from oracle import OracleCache, OraclePool, paged_decode
+    import workloads as wl
+    w = wl.llama13b_decode()
+    done = 0
+    with threadpool_limits(limits=1):
+        for b in bs:
+            k, v = w.kv(b)
+            L = int(w.lens[b])
+            nblk = -(-L // 16)
+            pool = OraclePool(nblk, 16)
+            cache = OracleCache(nblk, w.num_kv_heads, w.head_dim)
+            _, s = pool.seq_create()
+            _, slots, _ = pool.alloc_append(s, L)
+            cache.write(slots, k, v)
+            paged_decode(cache, [pool.table(s)], [L], w.q[b:b + 1], w.scale)
+            done += L * w.num_kv_heads * w.head_dim * 2 * 2
+    return done
+
+
+def cpu_baseline_pool(w, np, procs=None):
+    """The same oracle over all 64 sequences with a process pool (one
+    single-threaded process per core of the host share, 16 at most)."""
+    import multiprocessing as mp
+    procs = procs or max(1, min(16, len(os.sched_getaffinity(0))))
+    order = list(np.argsort(-w.lens))                  # longest first, dealt round robin
+    parts = [[int(b) for b in order[i::procs]] for i in range(procs)]
+    ctx = mp.get_context("spawn")                      # no fork of a process that holds the GPU
+    with ctx.Pool(procs) as pool:
+        pool.map(_oracle_warm, range(procs), chunksize=1)
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_seqs, parts, chunksize=1))
+        elapsed = time.perf_counter() - t0
+    return {"value": round(done / elapsed / 1e9, 5), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"all {w.batch} sequences, {procs} processes x 1 thread, float64 numpy, "
+                      f"{elapsed:.1f} s after worker start-up",
+            "seconds": round(elapsed, 2)}
 
 
 def cpu_baseline(w, np, target_s=15.0):
@@ -871,11 +965,15 @@ def main():
                           "pa_decode_hbm_frac": round(alg_bytes2 / (dec_ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "host": host_timings(w, pa, np),
     }
+    if not args.no_extras:
+        log("cold decode step")
+        res["cold_step"] = cold_step(pa, torch, np, w, d)
     del d
     torch.cuda.empty_cache()
     if not args.no_extras:
-        log("copy ceiling")
+        log("copy and read ceilings")
         res["ceiling"] = copy_ceiling(torch)
+        res["read_ceiling"] = read_ceiling(torch)
         log("decode e4m3")
         d8 = setup_decode(w, True, pa, torch, np)
         ms8, dec8 = run_decode(pa, torch, w, d8, args.steps, args.warmup)
@@ -909,6 +1007,9 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, np, args.cpu_seconds)
+        if not args.no_extras:
+            log("cpu baseline (oracle, process pool)")
+            res["cpu_baseline_pool"] = cpu_baseline_pool(w, np)
     print(json.dumps(res), flush=True)
 
 

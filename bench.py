@@ -18,6 +18,9 @@ Reported on one JSON line:
                (caches cold), an event pair per step: median, p10, p90
   ceiling      a plain device copy of 1 GiB (read + write GB/s), for context
   read_ceiling torch's fastest read-bound reduction over 1 GiB, for context
+  achievable_read  the library's read-only probe kernel with the decode's
+               access pattern (random 4 KiB tiles, 1.35 GB): the practical
+               read ceiling, and the step's fraction of it
   fp8_decode   the same batch with an e4m3 cache
   prefix_cow   32 sequences sharing an 800-token prompt: GB/s on unique and on
                logical K/V bytes
@@ -293,13 +296,33 @@ def read_ceiling(torch, nbytes=1 << 30, reps=20):
             "gbs_read": round(nbytes / (mean * 1e-3) / 1e9, 1), "ms": round(mean, 4)}
 
 
-def cold_step(pa, torch, np, w, d, reps=30):
+def achievable_read(pa, torch, np, reps=20, n_tiles=330000, per_wave=8):
+    """The library's read-only probe kernel (pa_probe_tile_gather) with the
+    decode's access pattern: 4 KiB tiles in a seeded random order over 1.35 GB,
+    8 tiles per wave, non-temporal loads -- the practical read ceiling."""
+    base = torch.empty(n_tiles * 4096, dtype=torch.uint8, device="cuda")
+    base.fill_(1)
+    ids = torch.from_numpy(np.random.default_rng(7).permutation(n_tiles).astype(np.int32)).cuda()
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    mean = time_events(torch, lambda: pa.pa_probe_tile_gather(base, ids, per_wave, sink), reps)
+    del base, ids, sink
+    nbytes = n_tiles * 4096
+    return {"kind": f"pa_probe_tile_gather: {n_tiles} 4 KiB tiles ({nbytes / 1e9:.2f} GB) in random order, "
+                    f"{per_wave} per wave, non-temporal loads",
+            "gbs_read": round(nbytes / (mean * 1e-3) / 1e9, 1), "ms": round(mean, 4)}
+
+
+def cold_step(pa, torch, np, w, d, reps=100, warmup=10):
     """The decode step with the caches flushed before every step: 512 MiB of
     unrelated writes (twice the 256 MB last-level cache) between steps, and an
     event pair around each step launch alone.  Per-launch event pairs read
     about 2 us long on this part, so this is a conservative figure."""
     junk = torch.empty(1 << 28, dtype=torch.float16, device="cuda")   # 512 MiB
     settle(torch, lambda: append_call(pa, w, d))
+    for _ in range(warmup):
+        junk.fill_(1.0)
+        append_call(pa, w, d)
+    torch.cuda.synchronize()
     ms = []
     for _ in range(reps):
         junk.fill_(1.0)
@@ -317,7 +340,7 @@ def cold_step(pa, torch, np, w, d, reps=30):
             "step_ms_p90": round(float(ms[(9 * len(ms)) // 10]), 5),
             "kv_gbs_median": round(kv / (med * 1e-3) / 1e9, 2),
             "hbm_frac_median": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "flush": "512 MiB fill between steps"}
+            "flush": "512 MiB fill between steps", "reps": reps, "warmup": warmup}
 
 
 def bench_prefix(pa, torch, np, workloads, reps):
@@ -614,6 +637,7 @@ def cpu_baseline_pool(w, np, procs=None):
         done = sum(pool.map(_oracle_seqs, parts, chunksize=1))
         elapsed = time.perf_counter() - t0
     return {"value": round(done / elapsed / 1e9, 5), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "tokens_per_s": round(w.batch / elapsed, 2),
             "sample": f"all {w.batch} sequences, {procs} processes x 1 thread, float64 numpy, "
                       f"{elapsed:.1f} s after worker start-up",
             "seconds": round(elapsed, 2)}
@@ -648,7 +672,7 @@ def cpu_baseline(w, np, target_s=15.0):
                 break
         elapsed = time.perf_counter() - t_start
     return {"value": round(done_bytes / elapsed / 1e9, 5), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "tokens_per_s": round(done_seqs / elapsed, 2),
             "sample": f"first {done_seqs} of {w.batch} sequences ({tokens} tokens, all 40 heads), "
                       f"{elapsed:.1f} s, float64 numpy, BLAS limited to 1 thread",
             "seconds": round(elapsed, 2)}
@@ -974,6 +998,10 @@ def main():
         log("copy and read ceilings")
         res["ceiling"] = copy_ceiling(torch)
         res["read_ceiling"] = read_ceiling(torch)
+        ach = achievable_read(pa, torch, np)
+        ach["step_frac"] = round(value / ach["gbs_read"], 4)
+        ach["roofline_kernel_frac"] = round(achieved / ach["gbs_read"], 4)
+        res["achievable_read"] = ach
         log("decode e4m3")
         d8 = setup_decode(w, True, pa, torch, np)
         ms8, dec8 = run_decode(pa, torch, w, d8, args.steps, args.warmup)
@@ -1010,6 +1038,10 @@ def main():
         if not args.no_extras:
             log("cpu baseline (oracle, process pool)")
             res["cpu_baseline_pool"] = cpu_baseline_pool(w, np)
+        for key in ("cpu_baseline", "cpu_baseline_pool"):
+            if key in res:
+                res[key]["host_cores"] = len(os.sched_getaffinity(0))
+                res[key]["gpu_over_oracle"] = round(value / res[key]["value"], 1)
     print(json.dumps(res), flush=True)
 
 

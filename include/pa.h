@@ -397,6 +397,21 @@ pa_status pa_prefill_chunk(const pa_kv_cache *cache, const void *q, int32_t num_
                            const int32_t *tables_dev, int32_t B, int32_t max_blocks,
                            int32_t max_chunk, float scale, float *out_dev, void *hip_stream);
 
+/* Measurement support, not part of the method: a read-only kernel with the
+ * decode's access pattern, for the achievable read bandwidth of that pattern.
+ * Wave w reads the 4 KiB tiles tile_ids[w * tiles_per_wave .. + tiles_per_wave)
+ * of base (tile i = bytes 4096 i .. 4096 i + 4095), 64 lanes x 16 bytes x 4 loads
+ * per tile, eight tiles in flight, non-temporal loads; ids are clamped into
+ * 0 .. base_bytes / 4096 - 1.  Nothing is written except, with negligible
+ * probability, 1 KiB of sink (a store that keeps the loads alive).
+ * base_dev: device, 16-byte aligned, base_bytes >= 4096.  tile_ids_dev: device
+ * int32[n_tiles].  tiles_per_wave: a positive multiple of 8 dividing n_tiles.
+ * sink_dev: device, 16-byte aligned, 1024 bytes.  Enqueued on hip_stream.
+ * Errors: BAD_ARG, HIP. */
+pa_status pa_probe_tile_gather(const void *base_dev, int64_t base_bytes, const int32_t *tile_ids_dev,
+                               int32_t n_tiles, int32_t tiles_per_wave, void *sink_dev,
+                               void *hip_stream);
+
 /* Message describing the last non-OK status on the calling thread ("" if none). */
 const char *pa_last_error(void);
 

@@ -124,6 +124,8 @@ _SIGNATURES = {
     "pa_mixed_step": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_int32, ctypes.c_float,
                                        ctypes.POINTER(pa_prefill_batch), ctypes.POINTER(pa_decode_batch),
                                        ctypes.c_void_p]),
+    "pa_probe_tile_gather": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_char_p, []),
 }
@@ -371,6 +373,18 @@ def pa_write_kv(cache: KvCache, k_new: torch.Tensor, v_new: torch.Tensor, slots:
                            _dev(v_new, torch.float16) if T else None,
                            _dev(slots, torch.int32) if T else None, T,
                            _p(pairs) if len(pairs) else None, len(pairs), _stream(stream)))
+
+
+def pa_probe_tile_gather(base: torch.Tensor, tile_ids: torch.Tensor, tiles_per_wave: int,
+                         sink: torch.Tensor, stream=None) -> None:
+    """Measurement support: reads the 4 KiB tiles of base (a contiguous CUDA
+    uint8 tensor) named by tile_ids (int32, device), tiles_per_wave per wave;
+    sink is a 1024-byte uint8 CUDA tensor."""
+    if sink.numel() < 1024:
+        raise PaError(PA_ERR_BAD_ARG, "pa_probe_tile_gather: sink must hold 1024 bytes")
+    _check(lib.pa_probe_tile_gather(_dev(base, torch.uint8), base.numel(), _dev(tile_ids, torch.int32),
+                                    int(tile_ids.numel()), int(tiles_per_wave), _dev(sink, torch.uint8),
+                                    _stream(stream)))
 
 
 def pa_decode_workspace_bytes(B: int, num_heads: int, head_dim: int, max_context_len: int) -> int:

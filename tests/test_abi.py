@@ -100,6 +100,15 @@ def test_device_entry_points_reject_bad_arguments_without_touching_a_gpu():
     st = pa.lib.pa_decode_append(ctypes.byref(d5), 16, 2, None, None, 16, 16, None, 1, 4, 16, 1.0, 16,
                                  16, 1 << 20, None, 0, None)
     assert st == pa.PA_ERR_BAD_ARG and b"k_new" in pa.lib.pa_last_error()
+    # the read probe: null buffers, a buffer under one tile, tiles_per_wave not
+    # a multiple of 8 or not dividing n_tiles; zero tiles is a no-op
+    probe = pa.lib.pa_probe_tile_gather
+    assert probe(None, 4096, 16, 8, 8, 16, None) == pa.PA_ERR_BAD_ARG
+    assert probe(16, 4095, 16, 8, 8, 16, None) == pa.PA_ERR_BAD_ARG
+    assert probe(16, 4096, 16, 12, 12, 16, None) == pa.PA_ERR_BAD_ARG
+    assert probe(16, 4096, 16, 20, 8, 16, None) == pa.PA_ERR_BAD_ARG
+    assert probe(16, 4096, None, 8, 8, 16, None) == pa.PA_ERR_BAD_ARG
+    assert probe(16, 4096, None, 0, 8, 16, None) == pa.PA_OK
 
 
 def test_workspace_size_formula():

@@ -1,0 +1,33 @@
+"""The read probe used for the achievable-bandwidth figure: it only reads
+(its buffer is unchanged and the sink stays zero), and ids outside the buffer
+are clamped into it."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_394_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+
+def test_probe_reads_only_and_clamps_ids():
+    n_base = 64
+    base = torch.arange(n_base * 4096, dtype=torch.int64, device="cuda").remainder(251).to(torch.uint8)
+    before = base.clone()
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, n_base, size=256).astype(np.int32)
+    ids[:8] = [-5, n_base, n_base + 1000, 2**31 - 1, -2**31, 0, n_base - 1, 17]
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    for per_wave in (8, 16, 256):
+        pa.pa_probe_tile_gather(base, torch.from_numpy(ids).cuda(), per_wave, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(base, before)
+    assert int(sink.count_nonzero()) == 0
+
+
+def test_probe_refuses_a_ragged_split():
+    base = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PaError):
+        pa.pa_probe_tile_gather(base, torch.zeros(12, dtype=torch.int32, device="cuda"), 8, sink)

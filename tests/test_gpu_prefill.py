@@ -59,6 +59,33 @@ def test_chunked_prefill_full_size_sampled():
                 close(got[int(case.cu_np[b]) + i, h], case.ref_row(b, i, h))
 
 
+def test_zero_row_chunks_inside_a_batch():
+    """Sequences with an empty chunk (a running sequence with nothing to
+    prefill) sit between others; their rows do not exist and the others'
+    outputs are unaffected."""
+    w = workloads.custom_prefill(151, [10, 400, 0, 33, 64], [25, 0, 130, 0, 1], 4, 2, 128)
+    check_all(PrefillCase(w))
+
+
+def test_more_than_64_sequences():
+    """Beyond 64 sequences the kernel takes sequence order as given instead of
+    ranking lengths within a wave: 70 sequences, short ragged chunks (some
+    empty) over priors of 0 .. 300 tokens."""
+    rng = np.random.default_rng(161)
+    prior = rng.integers(0, 300, size=70)
+    chunk = rng.integers(0, 24, size=70)
+    chunk[[0, 33, 69]] = [0, 130, 1]
+    w = workloads.custom_prefill(161, prior, chunk, 2, 1, 64)
+    check_all(PrefillCase(w))
+
+
+def test_long_prior_context():
+    """Chunks after 9000 and 8960 cached tokens (143 and 141 key tiles, odd
+    counts) and after 8990 (142 tiles, even), every row checked."""
+    w = workloads.custom_prefill(171, [9000, 8960, 8990], [100, 64, 98], 2, 2, 128)
+    check_all(PrefillCase(w))
+
+
 @pytest.mark.parametrize("scale", [-0.07, 0.0, 0.5])
 def test_prefill_any_finite_scale(scale):
     """The kernel keeps scores in raw units and scales inside the exponent; a

@@ -125,6 +125,20 @@ def test_per_sequence_paths(block_size, B, H, KVH, D, top):
     check(Twin(w, block_size=block_size))
 
 
+@pytest.mark.parametrize("B,H,KVH,D,top", [(80, 40, 8, 64, 400), (96, 8, 8, 128, 3000)])
+def test_more_than_64_sequences(B, H, KVH, D, top):
+    """Past 64 sequences the workgroups take batch order instead of the
+    longest-first ranking: one wide case on each decode path, with empty and
+    one-token contexts among them."""
+    rng = np.random.default_rng(331 + B)
+    lens = rng.integers(1, top, size=B)
+    lens[[3, 70]] = 0
+    lens[[5, 71]] = 1
+    w = workloads.custom_decode(331 + B, lens, H, KVH, D)
+    got = check(Twin(w))
+    assert np.all(got[3] == 0) and np.all(got[70] == 0)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_fp8_cache(D):
     lens = [1, 9, 64, 300, 1100, 2000]

@@ -750,9 +750,12 @@ batch through pa_decode after pa_write_kv; <128,1,4,0,4,1,16,1> the e4m3 step; <
 shared-prefix hint, so its row averages both); the block-size legs add the same kernels at block
 sizes 8, 32 and 64.  prefill_kernel<head_dim, block size> with 1280 workgroups is the 8 x 512-row
 chunked prefill; mixed_step_kernel runs that prefill and the 13B-shaped decode in one launch.
+tile_gather_kernel is the read probe of the achievable-bandwidth figure (pa_probe_tile_gather).
 
 One row per kernel and grid size (workgroups); rows under 0.2% of GPU time are left out.  Call
-counts include each leg's untimed settle phase.
+counts include each leg's untimed settle phase.  The step kernel's row also holds the cold-step
+leg's 110 calls (each after a 512 MiB fill), which raise its average by under 1 us against the
+timed warm steps.
 
 | kernel | workgroups | calls | average us | min us | max us | share of GPU time |
 |---|---|---|---|---|---|---|

@@ -737,7 +737,7 @@ def summarize_trace(trace_dir, bench_log, out_md):
     roof, pc, pf, f8 = b["roofline"], b.get("prefix_cow", {}), b.get("prefill", {}), b.get("fp8_decode", {})
     body = f"""# Kernel trace: bench.py on llama13b_decode (+ fp8, prefix-sharing, mixed, prefill, block-size legs)
 
-Commands (repository root, GPU box):
+Commands (repository root, on the MI355X):
 
     rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_decode -o run -- python -u bench.py --steps 20 --warmup 3 --no-cpu-baseline > gpurun_out/prof_decode.log
     python bench.py --summarize-trace gpurun_out/prof_decode gpurun_out/prof_decode.log {out_md}
@@ -827,7 +827,7 @@ def summarize_prefill_pmc(dir1, dir2, out_md):
     ]
     body = f"""# Chunked-prefill counters: prefill_kernel<128, 16, fp16>, 8 x 512-row chunks over 0..4096 cached tokens
 
-Commands (repository root, GPU box; one pass per counter set):
+Commands (repository root, on the MI355X; one pass per counter set):
 
     rocprofv3 --pmc {PREFILL_PMC_PASSES[0]} --output-format csv -d gpurun_out/pf_pmc1 -- python bench.py --prefill-only
     rocprofv3 --pmc {PREFILL_PMC_PASSES[1]} --output-format csv -d gpurun_out/pf_pmc2 -- python bench.py --prefill-only
@@ -880,7 +880,7 @@ def summarize_pmc(fetch_dir, write_dir):
     wr = per_call_w * w_scale * 1024.0
     text = f"""# Decode-step HBM traffic (pa_decode_append), llama13b_decode (64 seqs, L ~ U[1,2048], 40 x 128, fp16)
 
-Commands (from the repository root, on the GPU box):
+Commands (from the repository root, on the MI355X):
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- python bench.py --pmc-run
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- python bench.py --pmc-run

@@ -34,6 +34,8 @@ Reported on one JSON line:
                causal-valid FLOPs / time against the 2.5 PFLOP/s fp16 MFMA peak
   host         block-manager call times (admission per sequence, the step's
                batched reservation for all 64 sequences, table export)
+  capacity     13B-shaped requests that fit beside the weights: reserving the
+               maximum length per request against the library's block pool
   cpu_baseline the float64 oracle on a bounded sample of the batch (one core)
   cpu_baseline_pool  the same oracle over the whole batch in a pool of
                single-threaded processes (one per host core, 16 at most)
@@ -115,6 +117,46 @@ def pool_geometry(w, block_size, np):
         return w.num_blocks, w.init_free_order
     nb = -(-w.num_blocks * 16 // block_size) + w.batch + 8
     return nb, np.random.default_rng(1000 + w.seed + block_size).permutation(nb).astype(np.int32)
+
+
+def capacity(pa, np, hbm_bytes=288e9, weight_bytes=26e9, max_len=2048, block_size=16, seed=2048):
+    """How many requests of a Llama-2-13B-shaped model (40 layers x 40 KV heads
+    x 128 dims, fp16: 819,200 KV bytes a token) fit in the memory left after the
+    fp16 weights, admitted in arrival order until the first that does not fit:
+    reserving max_len tokens per request up front, against the library's block
+    pool (one block id spans every layer, so a block is 16 tokens of all
+    layers).  Request lengths are U[1, max_len], the decode workload's mix.
+    Host only; the same arithmetic for a 40 GB device is reported as context."""
+    per_token = 2 * 40 * 40 * 128 * 2
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, size=4096)
+
+    def fit(total_bytes):
+        budget = total_bytes - weight_bytes
+        naive = int(budget // (max_len * per_token))
+        n_blocks = int(budget // (block_size * per_token))
+        pool = pa.pa_pool_create(n_blocks, block_size, None)
+        admitted, tokens = 0, 0
+        for L in lens:
+            s = pa.pa_seq_create(pool)
+            try:
+                pa.pa_alloc_append(pool, s, int(L))
+            except pa.PaError as e:
+                if e.status != pa.PA_ERR_NO_BLOCKS:
+                    raise
+                break
+            admitted += 1
+            tokens += int(L)
+        used_blocks = n_blocks - pa.pa_pool_state(pool)[0]["free_blocks"]
+        return {"kv_budget_gb": round(budget / 1e9, 2), "blocks": n_blocks,
+                "reserve_max_len_fit": naive, "paged_fit": admitted,
+                "gain": round(admitted / max(naive, 1), 2),
+                "reserve_waste_frac": round(1 - float(lens[:naive].sum()) / (naive * max_len), 4) if naive else None,
+                "paged_waste_frac": round(1 - tokens / (used_blocks * block_size), 5) if used_blocks else None}
+
+    return {"workload": f"Llama-2-13B shape, {per_token} KV bytes a token, fp16 weights {weight_bytes / 1e9:.0f} GB, "
+                        f"requests U[1,{max_len}] tokens in arrival order, block {block_size}",
+            "mi355x_288gb": fit(hbm_bytes), "context_40gb_device": fit(40e9)}
 
 
 def host_timings(w, pa, np, trials=7):
@@ -991,6 +1033,7 @@ def main():
                           "pa_decode_gbs": round(alg_bytes2 / (dec_ms2 * 1e-3) / 1e9, 2),
                           "pa_decode_hbm_frac": round(alg_bytes2 / (dec_ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "host": host_timings(w, pa, np),
+        "capacity": capacity(pa, np),
     }
     if not args.no_extras:
         log("cold decode step")

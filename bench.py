@@ -1048,6 +1048,8 @@ def main():
         ach["step_frac"] = round(value / ach["gbs_read"], 4)
         ach["roofline_kernel_frac"] = round(achieved / ach["gbs_read"], 4)
         res["achievable_read"] = ach
+        # the same pattern at the e4m3 step's size (0.68 GB), for the fp8 leg below
+        res["achievable_read_fp8_size"] = achievable_read(pa, torch, np, n_tiles=165800)
         log("decode e4m3")
         d8 = setup_decode(w, True, pa, torch, np)
         ms8, dec8 = run_decode(pa, torch, w, d8, args.steps, args.warmup)
@@ -1056,6 +1058,9 @@ def main():
                              "kernel_ms": round(dec8, 5),
                              "kernel_gbs": round(alg8 / (dec8 * 1e-3) / 1e9, 2),
                              "hbm_frac": round(alg8 / (dec8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if "achievable_read_fp8_size" in res:
+            res["fp8_decode"]["achievable_frac"] = round(
+                res["fp8_decode"]["kernel_gbs"] / res["achievable_read_fp8_size"]["gbs_read"], 4)
         del d8
         torch.cuda.empty_cache()
         log("prefix sharing decode")

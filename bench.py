@@ -891,6 +891,79 @@ SQ counters sum over all SIMDs; GRBM_GUI_ACTIVE sums the 8 XCDs.
     print(body)
 
 
+DECODE_PMC_PASSES = (
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_VMEM SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_INSTS_SALU SQ_INSTS_SMEM SQ_INSTS_LDS "
+    "SQ_INST_LEVEL_VMEM GRBM_GUI_ACTIVE",
+)
+
+
+def summarize_decode_pmc(dir1, dir2, out_md):
+    """Counter summary of the decode-step kernel (pa_decode_append on the
+    13B-shaped batch) from two rocprofv3 --pmc runs of --pmc-run."""
+    def latest(d):
+        hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not hits:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        return max(hits, key=os.path.getmtime)
+
+    vals = {}
+    for d, names in zip((dir1, dir2), DECODE_PMC_PASSES):
+        path = latest(d)
+        for c in names.split():
+            table = _read_counter_csv(path, c)
+            keys = [k for k in table if "decode_seq_kernel" in k and "ILi128ELb0ELi2ELb0ELi4ELi1ELi16ELb1E" in k]
+            if not keys:
+                raise SystemExit(f"no decode-step dispatch with {c} in {path}")
+            v = table[keys[0]]
+            vals[c] = sum(v) / len(v)
+    xcds = 8
+    grbm = vals["GRBM_GUI_ACTIVE"] / xcds          # the counter sums the 8 XCDs
+    wave = vals["SQ_WAVE_CYCLES"]
+    alg = 1354661376                               # algorithmic bytes of one step launch
+    rows = [
+        ("kernel duration (GRBM_GUI_ACTIVE per XCD)", f"{grbm:,.0f} cycles"),
+        ("waves per dispatch", f"{vals['SQ_WAVES']:,.0f}"),
+        ("wave time issuing any instruction (ACTIVE_INST_ANY / WAVE_CYCLES)", f"{vals['SQ_ACTIVE_INST_ANY'] / wave:.3f}"),
+        ("wave time issuing VALU (ACTIVE_INST_VALU / WAVE_CYCLES)", f"{vals['SQ_ACTIVE_INST_VALU'] / wave:.3f}"),
+        ("wave time waiting on s_waitcnt (WAIT_ANY / WAVE_CYCLES)", f"{vals['SQ_WAIT_ANY'] / wave:.3f}"),
+        ("wave time waiting to issue (WAIT_INST_ANY / WAVE_CYCLES)", f"{vals['SQ_WAIT_INST_ANY'] / wave:.3f}"),
+        ("VMEM read instructions per dispatch", f"{vals['SQ_INSTS_VMEM_RD']:,.0f}"),
+        ("algorithmic bytes per VMEM read instruction", f"{alg / vals['SQ_INSTS_VMEM_RD']:,.0f}"),
+        ("VALU / SALU / SMEM / LDS instructions per VMEM read",
+         f"{vals['SQ_INSTS_VALU'] / vals['SQ_INSTS_VMEM_RD']:.1f} / {vals['SQ_INSTS_SALU'] / vals['SQ_INSTS_VMEM_RD']:.1f}"
+         f" / {vals['SQ_INSTS_SMEM'] / vals['SQ_INSTS_VMEM_RD']:.2f} / {vals['SQ_INSTS_LDS'] / vals['SQ_INSTS_VMEM_RD']:.3f}"),
+    ]
+    body = f"""# Decode-step counters: pa_decode_append, decode_seq_kernel<128,0,2,0,4,1,16,1>, llama13b_decode (64 seqs, L ~ U[1,2048], 40 x 128, fp16)
+
+Commands (repository root, on the MI355X; one pass per counter set):
+
+    rocprofv3 --pmc {DECODE_PMC_PASSES[0]} --output-format csv -d gpurun_out/dec_pmc1 -- python bench.py --pmc-run
+    rocprofv3 --pmc {DECODE_PMC_PASSES[1]} --output-format csv -d gpurun_out/dec_pmc2 -- python bench.py --pmc-run
+    python bench.py --summarize-decode-pmc gpurun_out/dec_pmc1 gpurun_out/dec_pmc2 {out_md}
+
+Averages over the {PMC_DECODE_STEPS} step launches of the run.  The SQ counters sum over all
+CUs; GRBM_GUI_ACTIVE sums the 8 XCDs.  The three wave-time shares (issuing, waiting on
+s_waitcnt, waiting to issue) are ratios of counters in the same units and sum to one.  Waves
+of this memory-bound kernel issue an instruction in under a tenth of their time; the rest they
+wait, on their own loads (s_waitcnt) or for the memory pipeline and the other waves of their
+SIMD to let the next load issue.  SQ_ACTIVE_INST_VMEM reads 0 on this part, and
+SQ_INST_LEVEL_VMEM gives no usable latency here; both stay in the raw list only.
+
+| quantity | value |
+|---|---|
+"""
+    for k, v in rows:
+        body += f"| {k} | {v} |\n"
+    body += "\nRaw per-dispatch averages:\n\n"
+    for k in sorted(vals):
+        body += f"- {k}: {vals[k]:,.0f}\n"
+    with open(out_md, "w") as f:
+        f.write(body)
+    print(body)
+
+
 def summarize_pmc(fetch_dir, write_dir):
     """Write the traffic summary from two rocprofv3 --pmc runs of --pmc-run."""
     def find(d):
@@ -957,6 +1030,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "BENCH_LOG", "OUT_MD"))
     ap.add_argument("--summarize-prefill-pmc", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "OUT_MD"))
+    ap.add_argument("--summarize-decode-pmc", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "OUT_MD"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -966,6 +1040,9 @@ def main():
         return
     if args.summarize_prefill_pmc:
         summarize_prefill_pmc(*args.summarize_prefill_pmc)
+        return
+    if args.summarize_decode_pmc:
+        summarize_decode_pmc(*args.summarize_decode_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library runs on a single MI355X and has no "

@@ -30,6 +30,24 @@ def test_mixed_step_matches_separate_calls_and_oracle(dlens):
     m.check_oracle(outp, outd)
 
 
+def test_mixed_step_wide_decode_batch_head_dim_64():
+    """80 decode sequences (beyond the 64 that are ranked by length inside a
+    wave, so they keep batch order), empty and one-token contexts among them,
+    beside a prefill batch with a zero-row chunk; head_dim 64, 8 heads."""
+    rng = np.random.default_rng(177)
+    dl = rng.integers(0, 900, size=80)
+    dl[[0, 41, 79]] = [0, 1, 2048]
+    wp = workloads.custom_prefill(177, [5, 300, 0, 900], [64, 0, 1, 300], 8, 8, 64)
+    wd = workloads.custom_decode(178, dl, 8, 8, 64)
+    m = Mixed(wp, wd)
+    outp, outd = m.run_mixed(wp.scale)
+    sp, sd = m.run_separate(wp.scale)
+    assert np.array_equal(outp, sp)
+    close(outd, sd.astype(np.float64))
+    assert np.all(outd[0] == 0)
+    m.check_oracle(outp, outd)
+
+
 def test_mixed_step_long_context_falls_back_to_two_launches():
     wp = workloads.custom_prefill(173, [20], [40], 2, 2, 64)
     wd = workloads.custom_decode(174, [17000, 15], 2, 2, 64)

@@ -30,6 +30,16 @@ def test_small_ragged_prefill(D):
     check_all(PrefillCase(w))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_prefill_eight_grouped_heads(D):
+    """Eight query heads over two KV heads (pairs of one sequence fill whole
+    XCD groups of ids) with ragged chunks: empty, one row, a partial last
+    tile, three tiles, and two sequences of equal total length."""
+    w = workloads.custom_prefill(181 + D, [127, 37, 300, 128, 0, 5, 171], [1, 21, 200, 0, 300, 129, 1],
+                                 8, 2, D)
+    check_all(PrefillCase(w))
+
+
 def test_grouped_heads_prefill():
     w = workloads.custom_prefill(111, [50, 3], [70, 130], 6, 2, 128)
     check_all(PrefillCase(w))

@@ -787,7 +787,7 @@ Commands (repository root, on the MI355X):
 Template arguments of the decode kernels: <head_dim, e4m3, units per step, pipelined, waves per
 workgroup, block-id registers, block size, appending>.  decode_seq_kernel<128,0,2,0,4,1,16,1> is
 the fp16 13B-shaped decode step (pa_decode_append, the roofline kernel) and <...,16,0> the same
-batch through pa_decode after pa_write_kv; <128,1,4,0,4,1,16,1> the e4m3 step; <128,0,2,0,8,1,16,0> the
+batch through pa_decode after pa_write_kv; <128,1,1,0,4,1,16,1> the e4m3 step; <128,0,2,0,8,1,16,0> the
 800-token shared-prompt decode (32 x 40 pairs, 8 waves per workgroup; timed without and with the
 shared-prefix hint, so its row averages both); the block-size legs add the same kernels at block
 sizes 8, 32 and 64.  prefill_kernel<head_dim, block size> with 1280 workgroups is the 8 x 512-row

@@ -370,7 +370,7 @@ constexpr int kUF16 = 2, kWpgF16 = 2;
 constexpr bool kPipeF16 = true;
 constexpr int kUF8 = 4, kWpgF8 = 1;
 constexpr bool kPipeF8 = false;
-constexpr int kSeqUF16 = 2, kSeqUF8 = 4;
+constexpr int kSeqUF16 = 2, kSeqUF8 = 1;
 constexpr bool kSeqPipeF16 = false, kSeqPipeF8 = false;
 constexpr int kSeqTR = 1;
 // The per-sequence path is taken when the batch alone fills the chip, at least

@@ -19,10 +19,10 @@ namespace {
 
 using namespace dev;
 
-// per-sequence decode inside the mixed launch: 2 units per step (4 for e4m3),
-// not pipelined, 4 waves (the standalone per-sequence configurations)
+// per-sequence decode inside the mixed launch: 2 units per step (1 for
+// e4m3), not pipelined, 4 waves (the standalone per-sequence configurations)
 template <bool FP8>
-constexpr int kMixU = FP8 ? 4 : 2;
+constexpr int kMixU = FP8 ? 1 : 2;
 constexpr int kMixW = 4;
 static_assert(kMixW * 64 == kThreads, "decode and prefill workgroups have one shape");
 

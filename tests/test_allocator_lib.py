@@ -176,6 +176,20 @@ def test_worked_example_and_config_scripts():
         t, ln = pa.pa_block_tables(p.lib, ids, max_blocks)
         st_, ot, oln = p.orc.block_tables(ids, max_blocks)
         assert t.tolist() == ot and ln.tolist() == oln
+    # the chunked-prefill script: per sequence, its prior context in one
+    # append, then its 512-token chunk in another
+    w = workloads.chunked_prefill()
+    p = Pair(w.num_blocks, 16, w.init_free_order)
+    for b in range(w.batch):
+        s = p.create()
+        for n in (int(w.prior[b]), int(w.chunk[b])):
+            st_, _, cow = p.append(s, n)
+            assert st_ == Status.OK and cow is None
+            p.check()
+    max_blocks = max(-(-int(L) // 16) for L in w.lens)
+    t, ln = pa.pa_block_tables(p.lib, list(range(w.batch)), max_blocks)
+    st_, ot, oln = p.orc.block_tables(list(range(w.batch)), max_blocks)
+    assert t.tolist() == ot and ln.tolist() == oln == w.lens.tolist()
     # the worked example's tables
     w = workloads.tiny_decode_worked_example()
     p = Pair(w.num_blocks, 16, w.init_free_order)

@@ -172,8 +172,8 @@ pa_status pa_append_tokens(pa_pool *pool, int32_t seq, const int32_t *tokens, in
  * tokens: host int32[n_tokens].  slots_out: host int32[n_tokens]; its first
  * n_tokens - *hit_tokens_out entries receive the slots of tokens *hit_tokens_out ..
  * n_tokens-1, the only ones whose K/V the caller must compute and write.
- * Keys are 64-bit FNV-1a hashes chained over the parent's key; a hit also
- * compares the stored parent key and token ids.
+ * A block's key is SHA-256 over its parent block's key and its token ids, so it
+ * names the whole prefix that ends with the block; a hit is a key match.
  * Errors: BAD_SEQ; BAD_ARG (sequence not empty, n_tokens < 0, NULL pointers);
  * NO_BLOCKS (reused blocks that wait in the queue count against it). */
 pa_status pa_alloc_prompt(pa_pool *pool, int32_t seq, const int32_t *tokens, int32_t n_tokens,

@@ -397,6 +397,8 @@ def _shape(t: torch.Tensor, shape, what: str) -> None:
 
 
 def _decode_shapes(cache: "KvCache", q, tables, lens, out, cached_blocks, what: str) -> None:
+    if q.dim() != 3:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: q must be [B][Hq][D]")
     B, Hq, D = q.shape
     if D != cache.head_dim:
         raise PaError(PA_ERR_BAD_ARG, f"{what}: q head_dim {D} != cache head_dim {cache.head_dim}")
@@ -408,6 +410,21 @@ def _decode_shapes(cache: "KvCache", q, tables, lens, out, cached_blocks, what: 
         _shape(cached_blocks, (B,), f"{what} cached_blocks")
 
 
+def _prefill_shapes(cache: "KvCache", q, cu_q, prior, tables, out, what: str) -> None:
+    if q.dim() != 3:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: q must be [sum C][Hq][D]")
+    total, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: q head_dim {D} != cache head_dim {cache.head_dim}")
+    if prior.dim() != 1:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: prior must be [B]")
+    B = int(prior.shape[0])
+    _shape(cu_q, (B + 1,), f"{what} cu_q")
+    if tables.dim() != 2 or tables.shape[0] != B:
+        raise PaError(PA_ERR_BAD_ARG, f"{what}: tables must be [B][max_blocks] with B = prior.numel()")
+    _shape(out, (total, Hq, D), f"{what} out")
+
+
 def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch.Tensor,
               max_context_len: int, scale: float, out: torch.Tensor,
               workspace: Optional[torch.Tensor] = None, stream=None,
@@ -415,8 +432,8 @@ def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch
     """q [B][Hq][D] float16, tables int32[B][max_blocks], lens int32[B] (device),
     out float32 [B][Hq][D], workspace a device byte tensor, cached_blocks None or
     device int32[B] (from pa_shared_prefix; a read hint, not an input)."""
-    B, Hq, D = q.shape
     _decode_shapes(cache, q, tables, lens, out, cached_blocks, "pa_decode")
+    B, Hq, D = q.shape
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     cb = None if cached_blocks is None else _dev(cached_blocks, torch.int32)
     _check(lib.pa_decode(ctypes.byref(cache.desc), _dev(q, torch.float16), Hq,
@@ -434,8 +451,8 @@ def pa_decode_append(cache: KvCache, q: torch.Tensor, k_new: torch.Tensor, v_new
     float16, device) written to the cache, and the step attends over the
     context ending with it.  Other arguments as pa_decode; cow_pairs as
     pa_write_kv."""
-    B, Hq, D = q.shape
     _decode_shapes(cache, q, tables, lens, out, cached_blocks, "pa_decode_append")
+    B, Hq, D = q.shape
     _shape(k_new, (B, cache.num_kv_heads, D), "pa_decode_append k_new")
     _shape(v_new, (B, cache.num_kv_heads, D), "pa_decode_append v_new")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
@@ -454,6 +471,7 @@ def pa_prefill_chunk(cache: KvCache, q: torch.Tensor, cu_q: torch.Tensor, prior:
                      stream=None) -> None:
     """q [sum C][Hq][D] float16, cu_q int32[B+1], prior int32[B], tables
     int32[B][max_blocks] (device), out float32 [sum C][Hq][D]."""
+    _prefill_shapes(cache, q, cu_q, prior, tables, out, "pa_prefill_chunk")
     total, Hq, D = q.shape
     B = int(prior.numel())
     _check(lib.pa_prefill_chunk(ctypes.byref(cache.desc), _dev(q, torch.float16), Hq, total,
@@ -469,6 +487,14 @@ def pa_swap_blocks(cache: "KvCache", host_k: torch.Tensor, host_v: torch.Tensor,
     pr = _i32(pairs).reshape(-1, 2)
     if host_k.device.type != "cpu" or host_v.device.type != "cpu" or host_k.shape != host_v.shape:
         raise PaError(PA_ERR_BAD_ARG, "host_k / host_v must be CPU tensors of one shape")
+    want = torch.uint8 if cache.fp8 else torch.float16
+    if host_k.dtype != want or host_v.dtype != want:
+        raise PaError(PA_ERR_BAD_ARG, f"pa_swap_blocks: host blocks must be {want}, like the cache")
+    if host_k.dim() != 4 or tuple(host_k.shape[1:]) != tuple(cache.k.shape[1:]):
+        raise PaError(PA_ERR_BAD_ARG, f"pa_swap_blocks: host blocks must be [n]{list(cache.k.shape[1:])}, "
+                                      f"got {list(host_k.shape)}")
+    if not (host_k.is_contiguous() and host_v.is_contiguous()):
+        raise PaError(PA_ERR_BAD_ARG, "pa_swap_blocks: host blocks must be contiguous")
     _check(lib.pa_swap_blocks(ctypes.byref(cache.desc), host_k.data_ptr(), host_v.data_ptr(),
                               int(host_k.shape[0]), _p(pr) if len(pr) else None, len(pr), direction,
                               _stream(stream)))
@@ -484,9 +510,22 @@ def pa_mixed_step(cache: "KvCache", scale: float, prefill: Optional[dict] = None
     optional workspace, cached_blocks) -- as pa_decode."""
     pb = db = None
     hq = None
+    # every shape is checked before any pointer is taken
+    if prefill is not None:
+        _prefill_shapes(cache, prefill["q"], prefill["cu_q"], prefill["prior"], prefill["tables"],
+                        prefill["out"], "pa_mixed_step prefill")
+        hq = int(prefill["q"].shape[1])
+    if decode is not None:
+        _decode_shapes(cache, decode["q"], decode["tables"], decode["lens"], decode["out"],
+                       decode.get("cached_blocks"), "pa_mixed_step decode")
+        hq_d = int(decode["q"].shape[1])
+        if hq is not None and hq_d != hq:
+            raise PaError(PA_ERR_BAD_ARG, f"pa_mixed_step: decode q has {hq_d} heads, prefill q {hq}; "
+                                          "one launch serves one head count")
+        hq = hq_d
     if prefill is not None:
         q = prefill["q"]
-        total, hq, _ = q.shape
+        total = int(q.shape[0])
         B = int(prefill["prior"].numel())
         pb = pa_prefill_batch(_dev(q, torch.float16), total, _dev(prefill["cu_q"], torch.int32),
                               _dev(prefill["prior"], torch.int32), _dev(prefill["tables"], torch.int32),
@@ -494,8 +533,7 @@ def pa_mixed_step(cache: "KvCache", scale: float, prefill: Optional[dict] = None
                               _dev(prefill["out"], torch.float32))
     if decode is not None:
         q = decode["q"]
-        B, hq_d, _ = q.shape
-        hq = hq_d if hq is None else hq
+        B = int(q.shape[0])
         ws = decode.get("workspace")
         cb = decode.get("cached_blocks")
         db = pa_decode_batch(_dev(q, torch.float16), _dev(decode["tables"], torch.int32),

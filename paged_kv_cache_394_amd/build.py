@@ -72,6 +72,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-only build of the block manager under AddressSanitizer and
+# UndefinedBehaviorSanitizer, for the CPU test tier.  It is compiled with the
+# host compiler (g++) from the two host sources only; nothing in it runs on a GPU.
+HOST_SOURCES = ("pool.cpp", "capi_host.cpp")
+HOST_SAN_LIB = os.path.join(BUILD, "libpa_host_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-I", INCLUDE, "-I", CSRC,
+           "-Wall", "-Wno-unused-function"] + SAN_FLAGS + \
+          [os.path.join(CSRC, n) for n in HOST_SOURCES] + ["-o", HOST_SAN_LIB]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ (sanitized host build) failed:\n{r.stdout}\n{r.stderr}")
+    return HOST_SAN_LIB
+
+
 def clean() -> None:
     shutil.rmtree(BUILD, ignore_errors=True)
     if os.path.exists(LIB):

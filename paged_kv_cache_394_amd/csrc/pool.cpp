@@ -3,6 +3,7 @@
 
 #include <unordered_map>
 
+#include <algorithm>
 #include <cstring>
 #include <new>
 
@@ -76,28 +77,23 @@ void BlockPool::unlink(int32_t b) {
   --nfree_;
 }
 
-// FNV-1a (64-bit) over the parent key (8 bytes, little endian) and the block's
-// token ids (4 bytes each, little endian).
-uint64_t BlockPool::block_hash(uint64_t parent, const int32_t* ids) const {
-  uint64_t h = 14695981039346656037ull;
-  auto mix = [&h](uint8_t byte) {
-    h ^= byte;
-    h *= 1099511628211ull;
-  };
-  for (int k = 0; k < 8; ++k) mix(static_cast<uint8_t>(parent >> (8 * k)));
+// SHA-256 over the parent's key (32 bytes) and the block's token ids (4 bytes
+// each, little endian).  The first block's parent key is 32 zero bytes.
+Digest BlockPool::block_key(const Digest& parent, const int32_t* ids) const {
+  Sha256 h;
+  h.update(parent.b, 32);
   for (int32_t i = 0; i < bs_; ++i) {
     const uint32_t t = static_cast<uint32_t>(ids[i]);
-    for (int k = 0; k < 4; ++k) mix(static_cast<uint8_t>(t >> (8 * k)));
+    const uint8_t le[4] = {static_cast<uint8_t>(t), static_cast<uint8_t>(t >> 8),
+                           static_cast<uint8_t>(t >> 16), static_cast<uint8_t>(t >> 24)};
+    h.update(le, 4);
   }
-  return h;
+  return h.finish();
 }
 
-int32_t BlockPool::lookup(uint64_t key, uint64_t parent, const int32_t* ids) const {
+int32_t BlockPool::lookup(const Digest& key) const {
   const auto it = cache_.find(key);
-  if (it == cache_.end()) return -1;
-  const Cached& c = cached_.at(it->second);
-  if (c.parent != parent || std::memcmp(c.ids.data(), ids, sizeof(int32_t) * bs_) != 0) return -1;
-  return it->second;
+  return it == cache_.end() ? -1 : it->second;
 }
 
 void BlockPool::push_back(int32_t b) {
@@ -301,11 +297,11 @@ Status BlockPool::alloc_prompt(int32_t seq, const int32_t* tokens, int32_t n, in
   }
   int64_t free_hits = 0;
   if (!cache_.empty() && n > 0) {
-    uint64_t parent = 0;
+    Digest parent{};
     for (int64_t i = 0; i < (n - 1) / bs_; ++i) {
       const int32_t* ids = tokens + i * bs_;
-      const uint64_t key = block_hash(parent, ids);
-      const int32_t b = lookup(key, parent, ids);
+      const Digest key = block_key(parent, ids);
+      const int32_t b = lookup(key);
       if (b < 0) break;
       hits.push_back(b);
       if (ref_[b] == 0) ++free_hits;
@@ -357,16 +353,16 @@ Status BlockPool::cache_commit(int32_t seq, int32_t* added, std::string* err) {
   const int64_t full = static_cast<int64_t>(s.tokens.size()) / bs_;
   std::vector<int32_t> done;  // blocks inserted, for the roll-back
   int32_t count = 0;
-  uint64_t parent = 0;
+  Digest parent{};
   try {
     for (int64_t i = 0; i < full; ++i) {
       const int32_t* ids = s.tokens.data() + i * bs_;
-      const uint64_t key = block_hash(parent, ids);
+      const Digest key = block_key(parent, ids);
       const int32_t b = s.table[i];
       // one cached copy per prefix; a block is cached under one prefix only
       if (cache_.find(key) == cache_.end() && cached_.find(b) == cached_.end()) {
         done.push_back(b);
-        cached_.emplace(b, Cached{key, parent, std::vector<int32_t>(ids, ids + bs_)});
+        cached_.emplace(b, Cached{key});
         cache_.emplace(key, b);
         ++count;
       }
@@ -395,7 +391,10 @@ Status BlockPool::fork(int32_t parent, int32_t* child) {
   try {
     c.table = seqs_[parent].table;
     c.tokens = seqs_[parent].tokens;
-    seqs_.reserve(seqs_.size() + 1);
+    // room for the child before any state changes; grows geometrically, like
+    // push_back would, so a run of forks does not move every record each time
+    if (seqs_.size() == seqs_.capacity())
+      seqs_.reserve(std::max<size_t>(2 * seqs_.capacity(), seqs_.size() + 1));
   } catch (const std::bad_alloc&) {
     return kCapacity;
   }

@@ -10,9 +10,10 @@
 //   * a reference count per block; a block returns to the queue at zero;
 //   * per sequence: a block table (logical -> physical) and a token count.
 // Prefix caching ([p2] "Deep dive", prefix-caching bullet; [p1] "Automatic
-// Prefix Caching (APC)"): a full block is keyed by a 64-bit chained hash of its
-// token ids and its parent block's key (FNV-1a over the parent key and the
-// block's ids); a hit is confirmed by comparing the stored parent key and ids.
+// Prefix Caching (APC)"): a full block is keyed by a chained digest of its
+// token ids and its parent block's key (SHA-256 over the parent's 32-byte key
+// and the block's ids), so a key names the whole token prefix that ends with
+// the block and a hit means that prefix matches (up to a SHA-256 collision).
 // Freed blocks keep their entry while they wait in the free queue and lose it
 // when the queue front hands them out again; a hit on a waiting block takes it
 // out of the middle of the queue.  Blocks enter the cache on cache_commit(),
@@ -30,6 +31,8 @@
 #include <string>
 #include <unordered_map>
 #include <vector>
+
+#include "sha256.hpp"
 
 namespace pa {
 
@@ -101,9 +104,9 @@ class BlockPool {
   void unlink(int32_t b);  // remove from the middle of the free queue
   int32_t host_pop();
   void host_push(int32_t h);
-  uint64_t block_hash(uint64_t parent, const int32_t* ids) const;
-  // cached block for this (parent key, ids), or -1
-  int32_t lookup(uint64_t key, uint64_t parent, const int32_t* ids) const;
+  Digest block_key(const Digest& parent, const int32_t* ids) const;
+  // cached block for this prefix key, or -1
+  int32_t lookup(const Digest& key) const;
 
   struct Seq {
     std::vector<int32_t> table;  // device blocks, or host blocks while swapped
@@ -113,8 +116,7 @@ class BlockPool {
     bool live = false;
   };
   struct Cached {
-    uint64_t key, parent;
-    std::vector<int32_t> ids;
+    Digest key;
   };
 
   int32_t n_, bs_;
@@ -125,7 +127,7 @@ class BlockPool {
   std::vector<int32_t> ref_;
   std::vector<Seq> seqs_;  // indexed by id; ids are never reused
   int64_t live_seqs_ = 0, tokens_ = 0, waste_ = 0, cow_copies_ = 0, shared_ = 0, refs_ = 0;
-  std::unordered_map<uint64_t, int32_t> cache_;   // key -> block
+  std::unordered_map<Digest, int32_t, DigestHash> cache_;   // prefix key -> block
   std::unordered_map<int32_t, Cached> cached_;    // block -> its entry
   int64_t prompt_tokens_ = 0, hit_tokens_ = 0, evictions_ = 0;
   // host swap space: FIFO free queue of host block ids

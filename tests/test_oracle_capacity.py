@@ -89,3 +89,26 @@ def test_internal_waste_bound():
         waste = pool.stats()["waste_tokens"]
         assert 0 <= waste <= g["max_internal_waste_tokens"]
         assert waste == nb * 16 - L
+
+
+def test_fit_rules_brute_force_on_small_lists():
+    """Both admission rules against a direct simulation of a pool on every
+    list of up to 4 lengths from {1, 16, 17, 40} and pools of 0..9 blocks."""
+    import itertools
+    for k in range(5):
+        for lens in itertools.product([1, 16, 17, 40], repeat=k):
+            for pool_blocks in range(10):
+                free, stop, skip, stopped = pool_blocks, [0, 0], [0, 0], False
+                free_skip = pool_blocks
+                for L in lens:
+                    need = -(-L // 16)
+                    if not stopped and need <= free:
+                        free -= need
+                        stop = [stop[0] + 1, stop[1] + need]
+                    else:
+                        stopped = True
+                    if need <= free_skip:
+                        free_skip -= need
+                        skip = [skip[0] + 1, skip[1] + need]
+                assert paged_fit_stop_at_first_failure(lens, pool_blocks, 16) == tuple(stop)
+                assert paged_fit_skip(lens, pool_blocks, 16) == tuple(skip)

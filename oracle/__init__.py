@@ -23,6 +23,8 @@ Pins (what each function is checked against, other than itself) live in
 from .allocator import OraclePool, Status  # noqa: F401
 from .attention import (  # noqa: F401
     attention_fp64,
+    attention_heads_fp64,
+    causal_chunk_fp64,
     dense_decode,
     paged_decode,
     paged_prefill,

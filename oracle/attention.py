@@ -49,6 +49,51 @@ def attention_fp64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
     return (p @ V) / p.sum()
 
 
+def attention_heads_fp64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """``attention_fp64`` for every query head of one sequence at once.
+
+    ``q`` [Hq][D]; ``K``/``V`` [L][Hkv][D], the sequence's rows in token order;
+    query head ``h`` reads KV head ``h // (Hq // Hkv)``.  Returns [Hq][D]
+    float64.  The same definition as ``attention_fp64``, with the per-head
+    products written as two batched matrix products (a library step).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Hq, D = q.shape
+    L, Hkv = K.shape[0], K.shape[1]
+    if L == 0:
+        return np.zeros((Hq, D), dtype=np.float64)
+    kv = np.arange(Hq) // (Hq // Hkv)
+    Kh = np.asarray(K, dtype=np.float64)[:, kv, :].transpose(1, 0, 2)   # [Hq][L][D]
+    Vh = np.asarray(V, dtype=np.float64)[:, kv, :].transpose(1, 0, 2)
+    s = np.matmul(Kh, q[:, :, None])[:, :, 0] * float(scale)           # [Hq][L]
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return np.matmul(p[:, None, :], Vh)[:, 0, :] / p.sum(axis=1)[:, None]
+
+
+def causal_chunk_fp64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, prior: int,
+                      scale: float) -> np.ndarray:
+    """One head of a chunk: row ``i`` of ``Q`` [C][D] sits at position
+    ``prior + i`` and attends to keys ``0 .. prior + i`` of ``K``/``V``
+    [prior + C][D] ([p1] "Mechanics of Chunked Prefill": full attention to the
+    cached prior context, causal inside the chunk).  All rows at once: the
+    scores of keys past a row's position are set to minus infinity before the
+    softmax, so they get weight zero.  Returns [C][D] float64.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    C, L = Q.shape[0], K.shape[0]
+    if C == 0:
+        return np.zeros((0, V.shape[1]), dtype=np.float64)
+    s = (Q @ K.T) * float(scale)                                        # [C][L]
+    visible = np.arange(L)[None, :] <= (int(prior) + np.arange(C))[:, None]
+    s = np.where(visible, s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
 class OracleCache:
     """Paged K/V arrays plus the two writes the path performs on them."""
 

@@ -5,7 +5,6 @@ held to the same bound against an oracle over the dequantised cache and to
 
 import numpy as np
 import pytest
-import torch
 
 import workloads
 from gpu_harness import ATOL8, DecodeCase, close, oracle_decode
@@ -117,40 +116,6 @@ def test_fp8_small_configs(make):
     case = DecodeCase(w, fp8=True, seqs=seqs)
     check_full(case, fp8_ref=(case.k_scale, case.v_scale))
     check_full(case, atol=ATOL8)
-
-
-def test_llama13b_full_size_sampled():
-    """The full 64-sequence, 40-head, lengths-up-to-2048 batch, checked on a
-    sample of (sequence, head) pairs, longest and shortest sequences included."""
-    w = workloads.llama13b_decode()
-    case = DecodeCase(w, poison=False)
-    got = case.decode()
-    order = np.argsort(w.lens)
-    rng = np.random.default_rng(5)
-    pairs = [(int(order[0]), 0), (int(order[-1]), 39), (int(order[-1]), 0), (int(order[1]), 17)]
-    pairs += [(int(i), int(h)) for i, h in zip(rng.integers(0, 64, 12), rng.integers(0, 40, 12))]
-    ref = oracle_decode(w, pairs)
-    for (i, h), r in ref.items():
-        close(got[i, h], r)
-    assert np.isfinite(got).all()
-
-
-def test_llama13b_fp8_sampled():
-    """Full batch in e4m3 (scales over all 64 sequences); sampled pairs against
-    the oracle over the dequantised cache (2e-3) and the fp16 source (5e-2)."""
-    w = workloads.llama13b_decode()
-    case = DecodeCase(w, fp8=True, poison=False)
-    got = case.decode()
-    order = np.argsort(w.lens)
-    pairs = [(int(order[0]), h) for h in (0, 39)] + [(int(order[-1]), 5)]
-    pairs += [(i, h) for i in range(0, 64, 5) for h in (0, 13, 39)]
-    ref = oracle_decode(w, pairs, None, (case.k_scale, case.v_scale))
-    for (i, h), r in ref.items():
-        close(got[i, h], r)
-    ref16 = oracle_decode(w, pairs)
-    for (i, h), r in ref16.items():
-        close(got[i, h], r, ATOL8, ATOL8)
-    assert np.isfinite(got).all()
 
 
 def test_wide_batch_beyond_64_sequences_per_sequence_path():

@@ -9,8 +9,7 @@ import torch
 
 import paged_kv_cache_394_amd as pa
 import workloads
-from gpu_harness import close
-from oracle import attention_fp64
+from gpu_harness import close, oracle_decode_all
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +33,9 @@ def build(w, small_heads=None):
     return pool, cache, seqs, n_cow
 
 
-# 40 heads: one workgroup per (sequence, head); 8 heads: the split path
-@pytest.mark.parametrize("prompt,heads", [(800, 40), (808, 40), (808, 8)])
+# 8 heads: the split path (40 heads, the per-sequence path, is checked on every
+# output in test_gpu_full_configs.py)
+@pytest.mark.parametrize("prompt,heads", [(800, 8), (808, 8)])
 def test_shared_prompt_decode(prompt, heads):
     w = workloads.prefix_cow(prompt_len=prompt, num_heads=heads)
     pool, cache, seqs, n_cow = build(w)
@@ -68,11 +68,5 @@ def test_shared_prompt_decode(prompt, heads):
     assert torch.equal(out, out_hint)
     got = out.cpu().numpy()
     pk, pv = w.prompt_kv()
-    rng = np.random.default_rng(prompt)
-    for b in list(range(0, w.batch, 5)) + [w.batch - 1]:
-        k, v = w.kv(b)
-        K = np.concatenate([pk, k]).astype(np.float64)
-        V = np.concatenate([pv, v]).astype(np.float64)
-        for h in rng.integers(0, w.num_heads, 3):
-            close(got[b, h], attention_fp64(w.q[b, h], K[:, h], V[:, h], w.scale))
-    assert np.isfinite(got).all()
+    rows = [(np.concatenate([pk, w.kv(b)[0]]), np.concatenate([pv, w.kv(b)[1]])) for b in range(w.batch)]
+    close(got, oracle_decode_all(w.q, lambda b: rows[b], w.batch, w.scale))

@@ -201,3 +201,69 @@ def test_prefill_chunk_split_equivalence():
     k, v = w.kv(0)
     row = dense_prefill_row(w.q[30, 1], k[:, 1], v[:, 1], 19 + 30, w.scale)
     assert np.array_equal(row, whole[30, 1])
+
+
+def test_all_heads_form_matches_sdpa_and_the_single_head_form():
+    """attention_heads_fp64 against torch's float64 SDPA (grouped heads expanded
+    by hand) and against attention_fp64 head by head."""
+    from oracle import attention_heads_fp64
+    rng = np.random.default_rng(31)
+    for L, Hq, Hkv, D in [(1, 4, 4, 8), (37, 8, 2, 64), (300, 6, 3, 128), (0, 2, 2, 4)]:
+        q = rng.standard_normal((Hq, D))
+        K = rng.standard_normal((L, Hkv, D))
+        V = rng.standard_normal((L, Hkv, D))
+        got = attention_heads_fp64(q, K, V, 0.2)
+        assert got.shape == (Hq, D)
+        if L == 0:
+            assert np.all(got == 0)
+            continue
+        g = Hq // Hkv
+        Ke = torch.from_numpy(np.repeat(K, g, axis=1).transpose(1, 0, 2).copy())   # [Hq][L][D]
+        Ve = torch.from_numpy(np.repeat(V, g, axis=1).transpose(1, 0, 2).copy())
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, :, None, :], Ke[None], Ve[None], scale=0.2)[0, :, 0].numpy()
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+        for h in range(Hq):
+            one = attention_fp64(q[h], K[:, h // g], V[:, h // g], 0.2)
+            assert np.allclose(got[h], one, rtol=1e-13, atol=1e-13)
+
+
+def test_causal_chunk_matches_masked_sdpa_and_row_form():
+    """causal_chunk_fp64 against torch SDPA with an explicit boolean mask
+    (row i sees keys 0..P+i), against dense_prefill_row row by row, and with
+    P = 0 against SDPA's own causal flag."""
+    from oracle import causal_chunk_fp64
+    rng = np.random.default_rng(32)
+    for P, C, D in [(0, 1, 8), (0, 40, 16), (33, 17, 64), (200, 129, 128)]:
+        Q = rng.standard_normal((C, D))
+        K = rng.standard_normal((P + C, D))
+        V = rng.standard_normal((P + C, D))
+        got = causal_chunk_fp64(Q, K, V, P, 0.3)
+        mask = torch.from_numpy(np.arange(P + C)[None, :] <= (P + np.arange(C))[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q)[None, None], torch.from_numpy(K)[None, None],
+            torch.from_numpy(V)[None, None], attn_mask=mask, scale=0.3)[0, 0].numpy()
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+        for i in (0, C // 2, C - 1):
+            assert np.allclose(got[i], dense_prefill_row(Q[i], K, V, P + i, 0.3), rtol=1e-13, atol=1e-13)
+        if P == 0:
+            causal = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(Q)[None, None], torch.from_numpy(K)[None, None],
+                torch.from_numpy(V)[None, None], is_causal=True, scale=0.3)[0, 0].numpy()
+            assert np.allclose(got, causal, rtol=1e-12, atol=1e-12)
+        # the last row sees every key: plain attention
+        assert np.allclose(got[-1], attention_fp64(Q[-1], K, V, 0.3), rtol=1e-13, atol=1e-13)
+
+
+def test_causal_chunk_planted_off_by_one_is_caught():
+    """A mask that lets row i see key P+i+1 (or hides key P+i) changes the
+    rows the SDPA comparison checks."""
+    from oracle import causal_chunk_fp64
+    rng = np.random.default_rng(33)
+    P, C, D = 5, 9, 8
+    Q, K, V = rng.standard_normal((C, D)), rng.standard_normal((P + C, D)), rng.standard_normal((P + C, D))
+    good = causal_chunk_fp64(Q, K, V, P, 0.3)
+    late = causal_chunk_fp64(Q, K, V, P + 1, 0.3)[:-1]
+    early = causal_chunk_fp64(Q, K, V, P - 1, 0.3)
+    assert not np.allclose(good[:-1], late, rtol=1e-6, atol=1e-6)
+    assert not np.allclose(good, early, rtol=1e-6, atol=1e-6)

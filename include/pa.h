@@ -353,6 +353,29 @@ pa_status pa_decode(const pa_kv_cache *cache, const void *q, int32_t num_heads,
                     int32_t max_context_len, float scale, float *out_dev, void *workspace_dev,
                     size_t workspace_bytes, void *hip_stream);
 
+/* Bytes of the static per-GPU scratch that pa_decode_noalloc uses in place of
+ * a workspace (16 MiB). */
+#define PA_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* pa_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and the same result bits, with the split path's partials in a static
+ * array of PA_DECODE_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends, instead of a caller workspace.  It calls no allocating routine.
+ * The caller still passes inputs and outputs, as for pa_decode.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (other streams, other threads) race; serialise them.  The array's earlier
+ * contents do not matter (each call writes every partial it reads).
+ * Errors: as pa_decode (no workspace errors), plus CAPACITY when
+ * pa_decode_workspace_bytes(B, num_heads, head_dim, max_context_len) exceeds
+ * PA_DECODE_SCRATCH_BYTES (nothing is launched; use pa_decode with a workspace),
+ * and HIP if the array's device address cannot be looked up. */
+pa_status pa_decode_noalloc(const pa_kv_cache *cache, const void *q, int32_t num_heads,
+                            const int32_t *tables_dev, const int32_t *lens_dev,
+                            const int32_t *cached_blocks_dev, int32_t B, int32_t max_blocks,
+                            int32_t max_context_len, float scale, float *out_dev,
+                            void *hip_stream);
+
 /* One decode step in one launch: append each sequence's new token to the
  * cache and attend over the context that ends with it ([p1] "PagedAttention
  * Mechanism" and [p2] "Deep dive": each generated token's K/V goes into the

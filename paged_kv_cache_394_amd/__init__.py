@@ -111,6 +111,10 @@ _SIGNATURES = {
                                    ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_decode_noalloc": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
     "pa_decode_append": (ctypes.c_int32, [ctypes.POINTER(pa_kv_cache), ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
@@ -440,6 +444,23 @@ def pa_decode(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch
                          _dev(tables, torch.int32), _dev(lens, torch.int32), cb, B, tables.shape[1],
                          max_context_len, scale, _dev(out, torch.float32), ws_ptr, ws_bytes,
                          _stream(stream)))
+
+
+PA_DECODE_SCRATCH_BYTES = 16 << 20
+
+
+def pa_decode_noalloc(cache: KvCache, q: torch.Tensor, tables: torch.Tensor, lens: torch.Tensor,
+                      max_context_len: int, scale: float, out: torch.Tensor, stream=None,
+                      cached_blocks: Optional[torch.Tensor] = None) -> None:
+    """pa_decode without a workspace: the split partials live in the library's
+    static per-GPU scratch (PA_DECODE_SCRATCH_BYTES).  Calls that overlap on
+    one GPU race."""
+    _decode_shapes(cache, q, tables, lens, out, cached_blocks, "pa_decode_noalloc")
+    B, Hq, D = q.shape
+    cb = None if cached_blocks is None else _dev(cached_blocks, torch.int32)
+    _check(lib.pa_decode_noalloc(ctypes.byref(cache.desc), _dev(q, torch.float16), Hq,
+                                 _dev(tables, torch.int32), _dev(lens, torch.int32), cb, B, tables.shape[1],
+                                 max_context_len, scale, _dev(out, torch.float32), _stream(stream)))
 
 
 def pa_decode_append(cache: KvCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

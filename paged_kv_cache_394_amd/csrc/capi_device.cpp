@@ -55,7 +55,7 @@ pa_status hip_status(hipError_t e, const char* fn) {
 pa_status check_decode(const pa::KvDesc& d, const std::string& fn, int32_t num_heads, const void* q,
                        const int32_t* tables_dev, const int32_t* lens_dev, int32_t B,
                        int32_t max_blocks, int32_t max_context_len, float scale,
-                       const float* out_dev, const void* workspace_dev, size_t workspace_bytes) {
+                       const float* out_dev) {
   if (num_heads < 1 || num_heads % d.num_kv_heads != 0)
     return fail(PA_ERR_BAD_ARG, fn + ": num_heads must be a positive multiple of num_kv_heads");
   if (B < 0 || max_blocks < 1 || max_context_len < 0)
@@ -68,6 +68,12 @@ pa_status check_decode(const pa::KvDesc& d, const std::string& fn, int32_t num_h
   if (!std::isfinite(scale)) return fail(PA_ERR_BAD_ARG, fn + ": scale must be finite");
   if (pa::decode_units(B, num_heads, max_context_len) > (int64_t(1) << 31) - 64)
     return fail(PA_ERR_BAD_ARG, fn + ": B * num_heads * ceil(max_context_len / 256) too large for one launch");
+  return PA_OK;
+}
+
+// The caller's workspace for pa_decode and its relatives (PA_OK when large enough).
+pa_status check_workspace(const pa::KvDesc& d, const std::string& fn, int32_t num_heads, int32_t B,
+                          int32_t max_context_len, const void* workspace_dev, size_t workspace_bytes) {
   const size_t need = pa::decode_workspace_bytes(B, num_heads, d.head_dim, max_context_len);
   if (workspace_bytes < need || (need > 0 && workspace_dev == nullptr))
     return fail(PA_ERR_BAD_ARG, fn + ": workspace smaller than pa_decode_workspace_bytes()");
@@ -151,12 +157,42 @@ pa_status pa_decode(const pa_kv_cache* cache, const void* q, int32_t num_heads,
   pa::KvDesc d;
   if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
   if (pa_status st = check_decode(d, fn, num_heads, q, tables_dev, lens_dev, B, max_blocks,
-                                  max_context_len, scale, out_dev, workspace_dev, workspace_bytes);
+                                  max_context_len, scale, out_dev);
+      st != PA_OK)
+    return st;
+  if (pa_status st = check_workspace(d, fn, num_heads, B, max_context_len, workspace_dev,
+                                     workspace_bytes);
       st != PA_OK)
     return st;
   if (B == 0) return pa::ok();
   return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, cached_blocks_dev, B,
                                       max_blocks, max_context_len, scale, out_dev, workspace_dev,
+                                      static_cast<hipStream_t>(hip_stream)),
+                    fn);
+}
+
+pa_status pa_decode_noalloc(const pa_kv_cache* cache, const void* q, int32_t num_heads,
+                            const int32_t* tables_dev, const int32_t* lens_dev,
+                            const int32_t* cached_blocks_dev, int32_t B, int32_t max_blocks,
+                            int32_t max_context_len, float scale, float* out_dev, void* hip_stream) {
+  const char* fn = "pa_decode_noalloc";
+  pa::KvDesc d;
+  if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
+  const size_t need = pa::decode_workspace_bytes(B, num_heads, d.head_dim, max_context_len);
+  if (need > pa::decode_scratch_capacity())
+    return fail(PA_ERR_CAPACITY, std::string(fn) + ": this batch needs " + std::to_string(need) +
+                                     " bytes of split partials, over the library's static " +
+                                     std::to_string(pa::decode_scratch_capacity()) +
+                                     "-byte scratch; use pa_decode with a workspace");
+  if (pa_status st = check_decode(d, fn, num_heads, q, tables_dev, lens_dev, B, max_blocks,
+                                  max_context_len, scale, out_dev);
+      st != PA_OK)
+    return st;
+  if (B == 0) return pa::ok();
+  void* ws = nullptr;
+  if (const hipError_t e = pa::decode_scratch(&ws); e != hipSuccess) return hip_status(e, fn);
+  return hip_status(pa::launch_decode(d, q, num_heads, tables_dev, lens_dev, cached_blocks_dev, B,
+                                      max_blocks, max_context_len, scale, out_dev, ws,
                                       static_cast<hipStream_t>(hip_stream)),
                     fn);
 }
@@ -171,7 +207,11 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* q, int32_t num_
   pa::KvDesc d;
   if (pa_status st = check_cache(cache, fn, &d); st != PA_OK) return st;
   if (pa_status st = check_decode(d, fn, num_heads, q, tables_dev, lens_dev, B, max_blocks,
-                                  max_context_len, scale, out_dev, workspace_dev, workspace_bytes);
+                                  max_context_len, scale, out_dev);
+      st != PA_OK)
+    return st;
+  if (pa_status st = check_workspace(d, fn, num_heads, B, max_context_len, workspace_dev,
+                                     workspace_bytes);
       st != PA_OK)
     return st;
   if (B > 0 && (k_new == nullptr || v_new == nullptr))
@@ -229,7 +269,11 @@ pa_status pa_mixed_step(const pa_kv_cache* cache, int32_t num_heads, float scale
   if (decode != nullptr) {
     const pa_decode_batch& q = *decode;
     if (pa_status st = check_decode(d, fn, num_heads, q.q, q.tables, q.lens, q.batch, q.max_blocks,
-                                    q.max_context_len, scale, q.out, q.workspace, q.workspace_bytes);
+                                    q.max_context_len, scale, q.out);
+        st != PA_OK)
+      return st;
+    if (pa_status st = check_workspace(d, fn, num_heads, q.batch, q.max_context_len, q.workspace,
+                                       q.workspace_bytes);
         st != PA_OK)
       return st;
   }

@@ -46,10 +46,22 @@
 //   split of kSplit blocks, and decode_reduce_kernel merging the splits'
 //   (max, sum, weighted V) partials.  Units are ordered longest first as well
 //   (full splits, then partial splits by decreasing size).
+#include <mutex>
+
 #include "decode_impl.hpp"
+
+// Partials of the split path for pa_decode_noalloc, which takes no workspace
+// from its caller: one array of kDecodeScratchBytes per GPU the library runs
+// on, held until the process ends.  Every launch on a GPU shares that GPU's
+// copy, so calls that overlap on one GPU race.  Nothing in it has to start at
+// zero: the merge reads only the partials the same call's split kernel wrote.
+static constexpr size_t kDecodeScratchBytes = PA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 namespace pa {
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
 
 using namespace dev;
 
@@ -453,6 +465,29 @@ hipError_t launch_decode_bs(const KvDesc& c, const void* q, int32_t Hq, const in
 }  // namespace
 
 int32_t decode_partition_tokens() { return kSplitTokens; }
+
+size_t decode_scratch_capacity() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // with dev current: the address of this GPU's copy of the array (the name
+    // itself is a host-side stand-in and must never reach a kernel)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len) {
   if (B <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0) return 0;

@@ -7,6 +7,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "pa.h"
+
 namespace pa {
 
 struct KvDesc {
@@ -27,6 +29,10 @@ hipError_t launch_write_kv(const KvDesc& c, const void* k_new, const void* v_new
 // Split-K decode: split kernel + split reduce.
 int32_t decode_partition_tokens();
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context_len);
+// The split path's partials in a static per-GPU array instead of a caller
+// workspace: its size, and this GPU's copy (looked up once per device).
+size_t decode_scratch_capacity();
+hipError_t decode_scratch(void** ptr);
 // Work units (one wave each) of one decode launch; must stay below 2^31.
 int64_t decode_units(int32_t B, int32_t Hq, int32_t max_context_len);
 // The new token of every sequence for an appending decode: k_new / v_new are

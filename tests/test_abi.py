@@ -118,3 +118,20 @@ def test_workspace_size_formula():
         nparts = -(-ctx // part)
         assert pa.pa_decode_workspace_bytes(B, H, D, ctx) == B * H * nparts * (D + 2) * 4
     assert pa.pa_decode_workspace_bytes(0, 1, 64, 16) == 0
+
+
+def test_noalloc_decode_refuses_oversize_batches_before_any_device_call():
+    """pa_decode_noalloc checks the split partials against its static scratch
+    first: with placeholder (never dereferenced) pointers, an oversize batch
+    returns CAPACITY on a host without a GPU."""
+    import paged_kv_cache_394_amd as pa
+    cache = pa.pa_kv_cache(256, 256, 64, 16, 8, 128, 0, 1.0, 1.0)
+    B, H, ctx = 16, 64, 1 << 16
+    assert pa.pa_decode_workspace_bytes(B, H, 128, ctx) > pa.PA_DECODE_SCRATCH_BYTES
+    st = pa.lib.pa_decode_noalloc(ctypes.byref(cache), 256, H, 256, 256, None, B, ctx // 16, ctx,
+                                  0.1, 256, None)
+    assert st == pa.PA_ERR_CAPACITY
+    assert b"scratch" in pa.lib.pa_last_error()
+    text = open(HEADER).read()
+    m = re.search(r"#define PA_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.PA_DECODE_SCRATCH_BYTES

@@ -8,9 +8,11 @@
 // (sequence, head).  The dispatcher hands out workgroups in id order, so the
 // decode workgroups start as soon as prefill workgroups retire: the
 // HBM-bound decode fills the CUs that the MFMA-bound prefill leaves idle in its
-// tail, instead of running after it.  Both halves are the standalone kernels'
-// bodies (prefill_body, decode_seq_body with 4 waves), bit-identical in result;
-// the decode half runs at the prefill's occupancy (2 workgroups per CU).
+// tail, instead of running after it.  Both halves are four-wave workgroup
+// bodies: prefill_body (the standalone prefill's body for e4m3 caches; for
+// fp16 caches the standalone launch uses an eight-wave kernel, equal within
+// rounding) and decode_seq_body (the standalone decode's, bit-identical in
+// result); the decode half runs at the prefill's occupancy (2 workgroups per CU).
 #include "decode_impl.hpp"
 #include "prefill_impl.hpp"
 

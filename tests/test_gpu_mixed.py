@@ -1,9 +1,11 @@
 """The mixed continuous-batching step (pa_mixed_step): prefill chunks and
 decode queries over one cache in one launch ([p1] "Chunked Prefill": chunks
-are batched with decode requests in the same step).  Its prefill half equals
-pa_prefill_chunk bit for bit (same workgroup body), and both halves match the
-float64 oracle; decode contexts past the one-launch limit fall back to two
-launches with the same results."""
+are batched with decode requests in the same step).  Its prefill half runs
+the 4-wave prefill workgroup body: bit for bit pa_prefill_chunk's result on an
+e4m3 cache (the same body there), and within the fp16 tolerance of it on an
+fp16 cache (where pa_prefill_chunk runs the 8-wave kernel).  Both halves match
+the float64 oracle; decode contexts past the one-launch limit fall back to two
+launches, the standalone kernels, with their results bit for bit."""
 
 import numpy as np
 import pytest
@@ -25,7 +27,7 @@ def test_mixed_step_matches_separate_calls_and_oracle(dlens):
     m = Mixed(wp, wd)
     outp, outd = m.run_mixed(wp.scale)
     sp, sd = m.run_separate(wp.scale)
-    assert np.array_equal(outp, sp)
+    close(outp, sp.astype(np.float64))
     close(outd, sd.astype(np.float64))
     m.check_oracle(outp, outd)
 
@@ -42,7 +44,7 @@ def test_mixed_step_wide_decode_batch_head_dim_64():
     m = Mixed(wp, wd)
     outp, outd = m.run_mixed(wp.scale)
     sp, sd = m.run_separate(wp.scale)
-    assert np.array_equal(outp, sp)
+    close(outp, sp.astype(np.float64))
     close(outd, sd.astype(np.float64))
     assert np.all(outd[0] == 0)
     m.check_oracle(outp, outd)

@@ -856,7 +856,7 @@ def summarize_trace(trace_dir, bench_log, out_md):
              "max": max(d), "total": sum(d)} for (n, w, c), d in groups.items()]
     rows.sort(key=lambda r: -r["total"])
     everything = sum(r["total"] for r in rows)
-    rows = [r for r in rows if r["total"] > 0.002 * everything]
+    rows = [r for r in rows if r["cold"] or r["total"] > 0.002 * everything]
     total = sum(r["total"] for r in rows)
     with open(bench_log) as f:
         b = json.loads([line for line in f if line.startswith("{")][-1])
@@ -879,8 +879,8 @@ chunked prefill over an fp16 cache, prefill_kernel<head_dim, block size, 1> with
 an e4m3 cache; mixed_step_kernel runs the prefill and the 13B-shaped decode in one launch.
 tile_gather_kernel is the read probe of the achievable-bandwidth figure (pa_probe_tile_gather).
 
-One row per kernel, grid size (workgroups) and cache state; rows under 0.2% of GPU time are left
-out.  "cold" rows hold the dispatches that directly follow the 1 GiB fill of a cold-timed leg
+One row per kernel, grid size (workgroups) and cache state; warm rows under 0.2% of GPU time are
+left out.  "cold" rows hold the dispatches that directly follow the 1 GiB fill of a cold-timed leg
 (the warm-up and timed steps of the headline step, of the e4m3 step and of the shared-prompt
 decode); "warm" rows the rest, including each leg's untimed settle phase.  The headline
 roofline's kernel time is the cold row of decode_seq_kernel<128,0,2,0,4,1,16,1>.

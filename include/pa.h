@@ -114,8 +114,10 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
 /* Release the pool's host memory.  NULL is ignored. */
 void pa_pool_destroy(pa_pool *pool);
 
-/* New empty sequence (length 0, empty table).  Ids are 0, 1, 2, ... in creation
- * order and are never reused. */
+/* New empty sequence (length 0, empty table): the per-request block list that
+ * draws from the shared pool ([p2] "Deep dive", the V1 structures: one block
+ * list per request; the lifecycle starts at admission with none).  Ids are 0,
+ * 1, 2, ... in creation order and are never reused. */
 pa_status pa_seq_create(pa_pool *pool, int32_t *seq_out);
 
 /* Make room for n_tokens new tokens of sequence seq ([p2] "Deep dive", lifecycle:
@@ -229,8 +231,12 @@ pa_status pa_fork_cow(pa_pool *pool, int32_t parent, int32_t *child_out);
 pa_status pa_seq_free(pa_pool *pool, int32_t seq);
 
 /* Export block tables for n sequences as a host int32[n][max_blocks] array padded
- * with -1, and lens_out int32[n] (may be NULL).  The caller copies them to the
- * device.  Errors: BAD_SEQ, BAD_ARG, CAPACITY (a table longer than max_blocks). */
+ * with -1, and lens_out int32[n] (may be NULL).  Row i is sequence seqs[i]'s block
+ * table: entry j is the physical block holding its logical block j ([p1] "Virtual
+ * Memory Paging Analogy": each sequence keeps an array from logical to physical
+ * block indices; [p1] "PagedAttention Mechanism": the kernel looks the blocks up
+ * there).  The caller copies them to the device.
+ * Errors: BAD_SEQ, BAD_ARG, CAPACITY (a table longer than max_blocks). */
 pa_status pa_block_tables(const pa_pool *pool, const int32_t *seqs, int32_t n,
                           int32_t max_blocks, int32_t *tables_out, int32_t *lens_out);
 
@@ -247,9 +253,11 @@ pa_status pa_seq_table(const pa_pool *pool, int32_t seq, int32_t *table_out, int
 pa_status pa_shared_prefix(const pa_pool *pool, const int32_t *seqs, int32_t n,
                            int32_t *blocks_out);
 
-/* Snapshot of the pool: counters, and optionally the free queue from front to back
- * (host int32[num_blocks], first free_blocks entries valid) and ref_cnt
- * (host int32[num_blocks]).  Either array may be NULL. */
+/* Snapshot of the pool ([p2] "Deep dive", the V1 structures: the free queue in
+ * eviction order and a ref_cnt per block): counters, and optionally the free
+ * queue from front to back (host int32[num_blocks], first free_blocks entries
+ * valid) and ref_cnt (host int32[num_blocks]).  stats_out and either array may
+ * be NULL.  Errors: BAD_ARG (pool NULL). */
 pa_status pa_pool_state(const pa_pool *pool, pa_pool_stats *stats_out,
                         int32_t *free_order_out, int32_t *ref_cnt_out);
 

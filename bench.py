@@ -561,14 +561,18 @@ def bench_preemption(pa, torch, np, workloads, reps=10):
             "recompute_attention_ms_per_layer": round(mean, 3)}
 
 
-def bench_mixed(pa, torch, np, workloads, reps):
+def bench_mixed(pa, torch, np, workloads, reps, fp8=False):
     """A continuous-batching step: the chunked-prefill batch (8 x 512 rows) and
     the 13B-shaped decode batch (64 sequences) over one cache, as one
-    pa_mixed_step launch against pa_prefill_chunk followed by pa_decode."""
+    pa_mixed_step call against pa_prefill_chunk followed by pa_decode."""
     wp, wd = workloads.chunked_prefill(), workloads.llama13b_decode()
     n = wp.num_blocks + wd.num_blocks
     pool = pa.pa_pool_create(n, 16)
-    cache = pa.KvCache(n, wd.num_kv_heads, wd.head_dim)
+    ks = vs = 1.0
+    if fp8:
+        (k1, v1), (k2, v2) = fp8_scales(wp, np), fp8_scales(wd, np)
+        ks, vs = max(k1, k2), max(v1, v2)
+    cache = pa.KvCache(n, wd.num_kv_heads, wd.head_dim, fp8=fp8, k_scale=ks, v_scale=vs)
     pids, dids = [], []
     for b in range(wp.batch):
         s = pa.pa_seq_create(pool)
@@ -606,7 +610,8 @@ def bench_mixed(pa, torch, np, workloads, reps):
 
     mixed_ms = time_events(torch, lambda: pa.pa_mixed_step(cache, scale, prefill, decode), reps)
     sep_ms = time_events(torch, separate, reps)
-    return {"workload": "chunked_prefill (8 x 512 rows) + llama13b_decode (64 seqs) over one cache",
+    return {"workload": "chunked_prefill (8 x 512 rows) + llama13b_decode (64 seqs) over one "
+                        f"{'e4m3' if fp8 else 'fp16'} cache",
             "mixed_ms": round(mixed_ms, 4), "separate_ms": round(sep_ms, 4),
             "speedup": round(sep_ms / mixed_ms, 3)}
 
@@ -1276,6 +1281,7 @@ def main():
         res["prefix_cache"] = bench_prefix_cache(pa, np, workloads)
         log("mixed prefill + decode step")
         res["mixed_step"] = bench_mixed(pa, torch, np, workloads, 20)
+        res["mixed_step_fp8"] = bench_mixed(pa, torch, np, workloads, 20, fp8=True)
         torch.cuda.empty_cache()
         log("preemption: swap vs recompute")
         res["preemption"] = bench_preemption(pa, torch, np, workloads)

@@ -22,6 +22,9 @@ Reported on one JSON line:
                step), one event pair over the K steps
   ceiling      a plain device copy of 1 GiB (read + write GB/s), for context
   read_ceiling torch's fastest read-bound reduction over 1 GiB, for context
+  achievable_mfma  the library's matrix-core probe (fp16 MFMAs on register
+               operands): the matrix throughput the part sustains, for context
+               beside the prefill's MFMA utilisation
   achievable_read  the library's read-only probe kernel with the decode's
                access pattern (random 4 KiB tiles, 1.35 GB): the practical
                read ceiling, and the step's fraction of it
@@ -366,6 +369,19 @@ def achievable_read(pa, torch, np, reps=20, n_tiles=330000, per_wave=8):
     return {"kind": f"pa_probe_tile_gather: {n_tiles} 4 KiB tiles ({nbytes / 1e9:.2f} GB) in random order, "
                     f"{per_wave} per wave, non-temporal loads",
             "gbs_read": round(nbytes / (mean * 1e-3) / 1e9, 1), "ms": round(mean, 4)}
+
+
+def achievable_mfma(pa, torch, n_workgroups=1024, iters=20000, reps=5):
+    """The library's matrix-core probe (pa_probe_mfma): fp16 16x16x32 MFMAs on
+    register operands, 4 waves per SIMD -- the fp16 matrix throughput the part
+    sustains, clock under matrix load included."""
+    sink = torch.zeros(64, dtype=torch.float32, device="cuda")
+    mean = time_events(torch, lambda: pa.pa_probe_mfma(n_workgroups, iters, sink), reps, warmup=2)
+    flop = float(n_workgroups) * iters * pa.PA_PROBE_MFMA_FLOP
+    tf = flop / (mean * 1e-3) / 1e12
+    return {"kind": f"pa_probe_mfma: {n_workgroups} x 4 waves, {iters} x 8 MFMAs a wave (fp16 16x16x32, "
+                    "register operands)",
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "ms": round(mean, 4)}
 
 
 FLUSH_BYTES = 1 << 30
@@ -1289,6 +1305,9 @@ def main():
         log("chunked prefill")
         res["prefill"] = bench_prefill(pa, torch, np, workloads, 20)
         torch.cuda.empty_cache()
+        log("achievable matrix-core rate (probe)")
+        res["achievable_mfma"] = achievable_mfma(pa, torch)
+        res["prefill"]["achievable_frac"] = round(res["prefill"]["tflops"] / res["achievable_mfma"]["tflops"], 4)
         log("chunked prefill, e4m3 cache")
         res["prefill_fp8"] = bench_prefill(pa, torch, np, workloads, 20, fp8=True)
         torch.cuda.empty_cache()

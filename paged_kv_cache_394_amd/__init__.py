@@ -130,6 +130,7 @@ _SIGNATURES = {
                                        ctypes.c_void_p]),
     "pa_probe_tile_gather": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "pa_probe_mfma": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_char_p, []),
 }
@@ -389,6 +390,17 @@ def pa_probe_tile_gather(base: torch.Tensor, tile_ids: torch.Tensor, tiles_per_w
     _check(lib.pa_probe_tile_gather(_dev(base, torch.uint8), base.numel(), _dev(tile_ids, torch.int32),
                                     int(tile_ids.numel()), int(tiles_per_wave), _dev(sink, torch.uint8),
                                     _stream(stream)))
+
+
+PA_PROBE_MFMA_FLOP = 16384 * 8 * 4   # per workgroup and iteration
+
+
+def pa_probe_mfma(n_workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """Measurement support: n_workgroups * iters * PA_PROBE_MFMA_FLOP FLOP of
+    fp16 MFMAs on register operands; sink is a 64-float CUDA tensor (unchanged)."""
+    if sink.numel() < 64:
+        raise PaError(PA_ERR_BAD_ARG, "pa_probe_mfma: sink must hold 64 floats")
+    _check(lib.pa_probe_mfma(int(n_workgroups), int(iters), _dev(sink, torch.float32), _stream(stream)))
 
 
 def pa_decode_workspace_bytes(B: int, num_heads: int, head_dim: int, max_context_len: int) -> int:

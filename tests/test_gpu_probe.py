@@ -1,6 +1,6 @@
-"""The read probe used for the achievable-bandwidth figure: it only reads
+"""The probes behind the achievable-rate figures.  The read probe only reads
 (its buffer is unchanged and the sink stays zero), and ids outside the buffer
-are clamped into it."""
+are clamped into it; the matrix-core probe writes nothing."""
 
 import numpy as np
 import pytest
@@ -31,3 +31,14 @@ def test_probe_refuses_a_ragged_split():
     sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
     with pytest.raises(pa.PaError):
         pa.pa_probe_tile_gather(base, torch.zeros(12, dtype=torch.int32, device="cuda"), 8, sink)
+
+
+def test_mfma_probe_writes_nothing():
+    sink = torch.zeros(64, dtype=torch.float32, device="cuda")
+    for n_wg, iters in ((1, 4), (16, 100), (0, 8), (4, 0)):
+        pa.pa_probe_mfma(n_wg, iters, sink)
+    torch.cuda.synchronize()
+    assert int(sink.count_nonzero()) == 0
+    for n_wg, iters in ((-1, 4), (1, 6)):
+        with pytest.raises(pa.PaError):
+            pa.pa_probe_mfma(n_wg, iters, sink)

@@ -447,8 +447,8 @@ pa_status pa_probe_tile_gather(const void *base_dev, int64_t base_bytes, const i
  * matrix cores with the chunked prefill's instruction (fp16 16x16x32 MFMA), for
  * the fp16 matrix throughput the device sustains.  n_workgroups workgroups of 4
  * waves; each wave issues iters * 8 MFMAs (8 independent accumulations) on
- * random-bit operands held in registers (the matrix cores' power, and so the
- * clock, depends on the bits): 16384 * 8 * iters * 4 * n_workgroups FLOP in all.
+ * random-bit operands held in registers, like real data:
+ * 16384 * 8 * iters * 4 * n_workgroups FLOP in all.
  * iters: a multiple of 4.  Nothing is written (sink_dev: device, 64 floats,
  * kept for a store the compiler cannot remove and no run takes).  Enqueued on
  * hip_stream.  Errors: BAD_ARG (NULL sink, negative sizes, iters not a

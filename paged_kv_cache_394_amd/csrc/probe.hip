@@ -63,8 +63,9 @@ constexpr int kMfmaChains = 8;
 constexpr int kMfmaOperands = 4;   // operand sets cycled through, iters is a multiple of this
 
 // A small fp16 value with random sign and mantissa bits (magnitude in
-// [2^-12, 2^-11)): operands that switch as many bits as real data do, since
-// the matrix cores' power, and with it the clock, depends on the bits.
+// [2^-12, 2^-11)): operands with the bit patterns of real data.  (The same
+// loop on constant operands measured 25% slower; which rate real operands get
+// is what the probe is for.)
 __device__ __forceinline__ half_t probe_value(uint32_t h) {
   h ^= h >> 16;
   h *= 0x7feb352du;

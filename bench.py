@@ -898,7 +898,8 @@ shared-prefix hint, so its row averages both); the block-size legs add the same 
 sizes 8, 32 and 64.  prefill_pp_kernel<head_dim, block size> with 640 workgroups is the 8 x 512-row
 chunked prefill over an fp16 cache, prefill_kernel<head_dim, block size, 1> with 1280 the same over
 an e4m3 cache; mixed_step_kernel runs the prefill and the 13B-shaped decode in one launch.
-tile_gather_kernel is the read probe of the achievable-bandwidth figure (pa_probe_tile_gather).
+tile_gather_kernel is the read probe of the achievable-bandwidth figure (pa_probe_tile_gather),
+mfma_loop_kernel the matrix-core probe of the achievable-MFMA figure (pa_probe_mfma).
 
 One row per kernel, grid size (workgroups) and cache state; warm rows under 0.2% of GPU time are
 left out.  "cold" rows hold the dispatches that directly follow the 1 GiB fill of a cold-timed leg

@@ -73,7 +73,7 @@ typedef struct {
   void *v_cache;          /* same shape as k_cache                                   */
   int32_t num_blocks;
   int32_t block_size;     /* tokens per block: 8, 16, 32 or 64 for the device calls  */
-  int32_t num_kv_heads;
+  int32_t num_kv_heads;   /* >= 1; one block (num_kv_heads*block_size*head_dim) < 2 GiB */
   int32_t head_dim;       /* 64 or 128                                               */
   int32_t dtype;          /* PA_KV_F16 or PA_KV_FP8_E4M3                             */
   float k_scale;          /* e4m3 only: stored code * k_scale = value                */

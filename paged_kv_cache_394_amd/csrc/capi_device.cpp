@@ -32,6 +32,10 @@ pa_status check_cache(const pa_kv_cache* c, const char* fn, pa::KvDesc* d) {
     return fail(PA_ERR_BAD_ARG, f + ": num_blocks * block_size must be < 2^31");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  // kernels form a block's byte offset from a 32-bit block size
+  if (static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim * 2 >= (int64_t(1) << 31))
+    return fail(PA_ERR_BAD_ARG, f + ": one cache block (num_kv_heads * block_size * head_dim "
+                                    "elements) must be < 2 GiB");
   if (c->dtype == PA_KV_FP8_E4M3 && c->block_size * c->head_dim < 1024)
     return fail(PA_ERR_UNSUPPORTED, f + ": an e4m3 (block, head) tile must be at least 1 KiB "
                                         "(block_size 8 needs head_dim 128)");

@@ -38,31 +38,6 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 // landed (vmcnt 0; the other counters are not waited on).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Copy one key tile (64 rows of one kv head) from the cache into an LDS
-// buffer.  Instruction i of wave w fills 16-byte slots 64 (w + kQW i) .. +63
-// of the tile: 64 / CPR consecutive rows, inside one block, so the block
-// lookup is wave-uniform; lane l loads the chunk the swizzle puts at slot
-// 64 (w + kQW i) + l.  Rows past the context read whatever their block holds.
-template <int D, int BS, bool KSWZ>
-__device__ __forceinline__ void dma_tile(half_t* buf, const half_t* __restrict__ cache,
-                                         const TileBlocks& tb, int64_t blk_stride, int kvh, int w,
-                                         int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int kInst = kBk * CPR / 64 / kQW;
-  static_assert(kInst >= 1 && kBk * CPR == 64 * kQW * kInst, "a tile is whole wave copies");
-#pragma unroll
-  for (int i = 0; i < kInst; ++i) {
-    const int slot0 = 64 * (w + kQW * i);
-    const int s = slot0 + lane;
-    const int r = s / CPR;
-    const int c = (s % CPR) ^ (KSWZ ? kswz<D>(r) : vswz<D>(r));
-    const int blk = (slot0 / CPR) / BS;
-    const half_t* src = cache + static_cast<int64_t>(pick_block(blk, tb)) * blk_stride +
-                        (kvh * BS + r % BS) * D + c * 8;
-    dma16(src, buf + slot0 * 8);
-  }
-}
-
 // Zero rows [first, 64) of a staged V tile: keys past the end get weight 0,
 // but stale cache rows may hold non-finite bits, and 0 * NaN is NaN.
 template <int D>
@@ -181,7 +156,46 @@ __device__ __forceinline__ void prefill_pp_body(
   const int ntiles = (n_keys + kBk - 1) / kBk;
   // tiles holding keys some row of this wave sees: 0 .. wtiles - 1
   const int wtiles = wq_last < wq_first ? 0 : min(ntiles, (P + wq_last) / kBk + 1);
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * BS * D;
+
+  // Staging copies.  Copy i of wave w fills 16-byte slots 64 (w + kQW i) ..
+  // + 63 of a tile: 64 / CPR consecutive rows, which lie inside block slot
+  // dslot[i] of the tile (wave-uniform).  Lane l copies the chunk that the
+  // swizzle puts at slot 64 (w + kQW i) + l, found kbo[i] (K) or vbo[i] (V)
+  // bytes into its block.  Both offsets are the same for every tile, so a copy
+  // costs a block lookup and a 64-bit add; a tile's block offsets are formed
+  // once, for its K copy, and reused for its V copy one step later.  Rows past
+  // the context read whatever their block holds.
+  constexpr int CPR = D / 8;
+  constexpr int NI = kBk * CPR / 64 / kQW;
+  static_assert(NI >= 1 && kBk * CPR == 64 * kQW * NI, "a tile is whole wave copies");
+  int dslot[NI];
+  uint32_t kbo[NI], vbo[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int s0 = 64 * (w + kQW * i);
+    const int r = (s0 + lane) / CPR, ch = (s0 + lane) % CPR;
+    dslot[i] = (s0 / CPR) / BS;
+    const uint32_t row = static_cast<uint32_t>((kvh * BS + r % BS) * D);
+    kbo[i] = 2u * (row + ((ch ^ kswz<D>(r)) << 3));
+    vbo[i] = 2u * (row + ((ch ^ vswz<D>(r)) << 3));
+  }
+  // bytes per cache block: below 2^31 (checked when the cache is described)
+  const uint32_t blk_bytes = 2u * static_cast<uint32_t>(Hkv * BS * D);
+  // byte offsets of the blocks this wave copies, for the tile whose table
+  // entries lanes 0 .. kBk / BS - 1 of ids hold
+  auto block_offsets = [&](int ids, uint64_t (&bo)[NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int id = clamp_id(__builtin_amdgcn_readlane(ids, dslot[i]), num_blocks);
+      bo[i] = static_cast<uint64_t>(static_cast<uint32_t>(id)) * blk_bytes;
+    }
+  };
+  auto copy_tile = [&](half_t* buf, const half_t* cache, const uint64_t (&bo)[NI],
+                       const uint32_t (&lo)[NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      dma16(reinterpret_cast<const char*>(cache) + bo[i] + lo[i], buf + 64 * (w + kQW * i) * 8);
+  };
 
   // Per-lane byte offsets of the MFMA operand reads.  K: as in prefill_body.
   // V^T (the A operand of O^T = V^T P^T) by transpose loads: for 32-key pair
@@ -317,13 +331,17 @@ __device__ __forceinline__ void prefill_pp_body(
   };
 
   // Prologue: K of tile 0 into LDS.
+  uint64_t bo_v[NI];  // blocks of tile t, for its V copy in step t
+  {
+    const int ids0 = tile_ids_lanes<BS>(trow, 0, max_blocks, lane);
+    wait_loads();
+    block_offsets(ids0, bo_v);
+  }
   if (ntiles > 0) {
-    dma_tile<D, BS, true>(sK0, kc, tile_blocks<BS>(trow, 0, max_blocks, num_blocks), blk_stride, kvh, w,
-                          lane);
+    copy_tile(sK0, kc, bo_v, kbo);
     wait_loads();
   }
   int ids_k = tile_ids_lanes<BS>(trow, 1, max_blocks, lane);  // tile t + 1, for K
-  int ids_v = tile_ids_lanes<BS>(trow, 0, max_blocks, lane);  // tile t, for V
   __syncthreads();
 
   // Step t = phases 2 t and 2 t + 1 (PAR = t % 2): tile t's K is in K buffer
@@ -335,11 +353,12 @@ __device__ __forceinline__ void prefill_pp_body(
     using CP = std::integral_constant<int, PAR>;
     using CQ = std::integral_constant<int, 1 - PAR>;
     // copies for the next step: K of tile t + 1, V of tile t
-    dma_tile<D, BS, true>(PAR ? sK0 : sK1, kc, tile_blocks_from<BS>(ids_k, num_blocks), blk_stride, kvh,
-                          w, lane);
-    dma_tile<D, BS, false>(PAR ? sV1 : sV0, vc, tile_blocks_from<BS>(ids_v, num_blocks), blk_stride, kvh,
-                           w, lane);
-    ids_v = ids_k;
+    uint64_t bo_k[NI];
+    block_offsets(ids_k, bo_k);
+    copy_tile(PAR ? sK0 : sK1, kc, bo_k, kbo);
+    copy_tile(PAR ? sV1 : sV0, vc, bo_v, vbo);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) bo_v[i] = bo_k[i];
     ids_k = tile_ids_lanes<BS>(trow, t + 2, max_blocks, lane);
     // the matrix phase of a set: P.V of tile t - 1, then the scores of tile t
     auto matrix = [&]() __attribute__((always_inline)) {

@@ -82,6 +82,9 @@ def test_device_entry_points_reject_bad_arguments_without_touching_a_gpu():
     d3 = pa.pa_kv_cache(16, 16, 1 << 27, 16, 1, 128, 0, 1.0, 1.0)
     st = pa.lib.pa_write_kv(ctypes.byref(d3), None, None, None, 0, None, 0, None)
     assert st == pa.PA_ERR_BAD_ARG and b"2^31" in pa.lib.pa_last_error()
+    d3 = pa.pa_kv_cache(16, 16, 4, 64, 1 << 17, 128, 0, 1.0, 1.0)
+    st = pa.lib.pa_write_kv(ctypes.byref(d3), None, None, None, 0, None, 0, None)
+    assert st == pa.PA_ERR_BAD_ARG and b"2 GiB" in pa.lib.pa_last_error()
     d4 = pa.pa_kv_cache(16, 16, 4, 16, 1, 128, 1, 0.0, 1.0)
     st = pa.lib.pa_write_kv(ctypes.byref(d4), None, None, None, 0, None, 0, None)
     assert st == pa.PA_ERR_BAD_ARG

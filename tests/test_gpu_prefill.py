@@ -84,11 +84,13 @@ def test_long_prior_context():
     check_all(PrefillCase(w))
 
 
-@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.5])
-def test_prefill_any_finite_scale(scale):
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.5, 0.9, 2.0, -3.0])
+def test_prefill_any_finite_scale(scale, D):
     """The kernel keeps scores in raw units and scales inside the exponent; a
-    negative scale flips q, a zero scale gives the mean of the visible values."""
-    w = workloads.custom_prefill(131, [20, 0], [40, 70], 2, 2, 128)
+    negative scale flips q, a zero scale gives the mean of the visible values,
+    and large scales make the weights nearly one-hot."""
+    w = workloads.custom_prefill(131, [20, 0], [40, 70], 2, 2, D)
     check_all(PrefillCase(w), scale)
 
 

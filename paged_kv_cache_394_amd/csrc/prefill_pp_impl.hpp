@@ -370,7 +370,9 @@ __device__ __forceinline__ void prefill_pp_body(
     } else {
       if (t >= 1 && t - 1 < wtiles) softmax(t - 1);
     }
-    __syncthreads();
+    // keeps the sets in step; orders no memory (nothing a wave reads in this
+    // step is written in it), so the copies issued above stay in flight
+    __builtin_amdgcn_s_barrier();
     if constexpr (SET == 0) {
       if (t < wtiles) softmax(t);
     } else {
